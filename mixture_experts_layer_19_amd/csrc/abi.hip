@@ -1,0 +1,462 @@
+// abi.hip -- the C ABI of libmoe (declared in include/moe.h).
+//
+// Argument checking, workspace layout, weight packing entry, and the layer
+// schedule.  The two-stream schedule follows the Hy3 on CANN NPU guide,
+// section 8.5 (the shared expert is issued to a second stream whose start is
+// ordered after Gating on the main stream; the main stream runs the routed
+// path and waits for the shared expert before the final add) and the
+// HunyuanImage-3.0 multi-stream article (the side stream is created once and
+// handed to the module at construction, part 1-2; an input-ready event
+// recorded on the main stream is awaited by the side stream, and a
+// shared-done event recorded on the side stream is awaited by the main stream
+// before output = shared + combined, part 3).
+#include <hip/hip_runtime.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "moe_common.hpp"
+#include "moe_launch.hpp"
+
+struct moe_ctx {
+  int device;
+  hipStream_t side;
+  hipEvent_t ev_ready;   // recorded on the caller's stream after gating
+  hipEvent_t ev_done;    // recorded on the side stream after the shared expert
+  char last_error[256];
+};
+
+namespace {
+
+using namespace moe;
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+
+int fmt_of(int dtype) {
+  return dtype == MOE_F32 ? FMT_F32 : dtype == MOE_BF16 ? FMT_BF16 : FMT_MX8;
+}
+size_t elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1; }
+int chunk_elems(int dtype) { return dtype == MOE_F32 ? 64 : dtype == MOE_BF16 ? 128 : 256; }
+
+// Shape and dtype checks shared by every entry point.
+moe_status check_desc(const moe_desc *d) {
+  if (!d) return MOE_ERR_INVALID_ARG;
+  if (d->hidden <= 0 || d->num_experts <= 0 || d->num_experts > 1024 || d->top_k <= 0 ||
+      d->top_k > 16 || d->top_k > d->num_experts || d->inter <= 0 || d->shared_inter < 0)
+    return MOE_ERR_INVALID_ARG;
+  if (d->route_norm != 0 && d->route_norm != 1) return MOE_ERR_INVALID_ARG;
+  for (int v : {d->act_dtype, d->expert_dtype, d->out_dtype})
+    if (v < MOE_F32 || v > MOE_MXFP8) return MOE_ERR_INVALID_ARG;
+  const bool f32 = d->act_dtype == MOE_F32 && d->expert_dtype == MOE_F32 && d->out_dtype == MOE_F32;
+  const bool b16 = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_BF16 && d->out_dtype == MOE_BF16;
+  const bool mx = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_MXFP8 && d->out_dtype == MOE_BF16;
+  if (!(f32 || b16 || mx)) return MOE_ERR_UNSUPPORTED;
+  // K chunks of 256 bytes; output tiles of 256 rows / 16-block groups
+  const int im = mx ? 256 : 128;
+  if (d->hidden % 256 || d->inter % im || d->shared_inter % im) return MOE_ERR_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Layout of one call's workspace.  All offsets 256-byte aligned.
+struct Layout {
+  size_t logits, idx, w, counts, offsets, src, dest, perm, xq, xs, h, hs, sh_h, sh_hs, y, z, total;
+};
+
+Layout layout(const moe_desc *d, int T, int which) {
+  Layout L;
+  memset(&L, 0, sizeof L);
+  const size_t P = (size_t)T * d->top_k, E = d->num_experts, H = d->hidden;
+  const size_t I = d->inter, Is = d->shared_inter;
+  const bool mx = d->expert_dtype == MOE_MXFP8;
+  const size_t eh = elem_bytes(d->expert_dtype), eo = elem_bytes(d->out_dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
+  const bool layer = which == MOE_WS_LAYER;
+  if (which == MOE_WS_ROUTE || layer) L.logits = take((size_t)T * E * 4);
+  if (layer) {
+    L.idx = take(P * 4);
+    L.w = take(P * 4);
+    L.counts = take(E * 4);
+    L.offsets = take((E + 1) * 4);
+    L.src = take(P * 4);
+    L.dest = take(P * 4);
+  }
+  if (which == MOE_WS_PERMUTE || layer) L.perm = take(permute_ws_bytes(T, (int)E));
+  const bool routed = which == MOE_WS_GROUPED_FFN || layer;
+  const bool shared = (which == MOE_WS_SHARED_FFN || layer) && Is > 0;
+  if (mx && (routed || shared)) {
+    L.xq = take((size_t)T * H);
+    L.xs = take((size_t)T * H / 32);
+  }
+  if (routed) {
+    L.h = take(P * I * eh);
+    if (mx) L.hs = take(P * I / 32);
+  }
+  if (shared) {
+    L.sh_h = take((size_t)T * Is * eh);
+    if (mx) L.sh_hs = take((size_t)T * Is / 32);
+  }
+  if (layer) {
+    L.y = take(P * H * eo);
+    if (Is > 0) L.z = take((size_t)T * H * eo);
+  }
+  L.total = off;
+  return L;
+}
+
+moe_status device_error(moe_ctx *ctx, hipError_t err, const char *where) {
+  if (ctx) snprintf(ctx->last_error, sizeof ctx->last_error, "%s: %s", where, hipGetErrorString(err));
+  return MOE_ERR_DEVICE;
+}
+
+moe_status check_ctx(moe_ctx *ctx) {
+  if (!ctx) return MOE_ERR_INVALID_ARG;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev != ctx->device) return MOE_ERR_INVALID_ARG;
+  return MOE_OK;
+}
+
+// One expert FFN (routed or shared) given activations already in the expert
+// format (xa: x itself for f32/bf16, the MX codes for MX-fp8).
+hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *xa,
+               const uint8_t *xs, int T, const int32_t *sorted_src, const int32_t *offsets,
+               void *y, void *h, uint8_t *hs, hipStream_t s) {
+  const int F = fmt_of(d->expert_dtype);
+  const int H = d->hidden, I = shared ? d->shared_inter : d->inter;
+  const int E = shared ? 1 : d->num_experts;
+  const int rows = shared ? T : T * d->top_k;
+  const size_t eb = elem_bytes(d->expert_dtype);
+  const int ce = chunk_elems(d->expert_dtype);
+
+  GemmArgs g1;
+  memset(&g1, 0, sizeof g1);
+  g1.w = (const uint8_t *)(shared ? w->sh_gate_up : w->gate_up);
+  g1.w_scale = (const uint16_t *)(shared ? w->sh_gate_up_scale : w->gate_up_scale);
+  g1.w_expert_stride = (size_t)(2 * I / 16) * (H / ce) * kBlockBytes;
+  g1.ws_expert_stride = (size_t)(2 * I / 16) * (H / ce) * 64;
+  g1.a = (const uint8_t *)xa;
+  g1.a_scale = xs;
+  g1.a_row_bytes = (long long)H * eb;
+  g1.sorted_src = shared ? nullptr : sorted_src;
+  g1.k_route = d->top_k;
+  g1.offsets = shared ? nullptr : offsets;
+  g1.rows = rows;
+  g1.E = E;
+  g1.N = 2 * I;
+  g1.K = H;
+  g1.out = h;
+  g1.out_scale = hs;
+  g1.n_out = I;
+  hipError_t err = launch_grouped_gemm(g1, F, EPI_SWIGLU, F, rows, s);
+  if (err != hipSuccess) return err;
+
+  GemmArgs g2;
+  memset(&g2, 0, sizeof g2);
+  g2.w = (const uint8_t *)(shared ? w->sh_down : w->down);
+  g2.w_scale = (const uint16_t *)(shared ? w->sh_down_scale : w->down_scale);
+  g2.w_expert_stride = (size_t)(H / 16) * (I / ce) * kBlockBytes;
+  g2.ws_expert_stride = (size_t)(H / 16) * (I / ce) * 64;
+  g2.a = (const uint8_t *)h;
+  g2.a_scale = hs;
+  g2.a_row_bytes = (long long)I * eb;
+  g2.sorted_src = nullptr;
+  g2.k_route = d->top_k;
+  g2.offsets = shared ? nullptr : offsets;
+  g2.rows = rows;
+  g2.E = E;
+  g2.N = H;
+  g2.K = I;
+  g2.out = y;
+  g2.out_scale = nullptr;
+  g2.n_out = H;
+  return launch_grouped_gemm(g2, F, EPI_PLAIN, fmt_of(d->out_dtype), rows, s);
+}
+
+bool weights_ok(const moe_desc *d, const moe_weights *w, int need_router, int need_routed,
+                int need_shared) {
+  if (!w) return false;
+  const bool mx = d->expert_dtype == MOE_MXFP8;
+  if (need_router && !w->router_w) return false;
+  if (need_routed && (!w->gate_up || !w->down || (mx && (!w->gate_up_scale || !w->down_scale))))
+    return false;
+  if (need_shared && d->shared_inter > 0 &&
+      (!w->sh_gate_up || !w->sh_down || (mx && (!w->sh_gate_up_scale || !w->sh_down_scale))))
+    return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+    case MOE_ERR_WORKSPACE: return "workspace too small";
+    case MOE_ERR_DEVICE: return "device (HIP) error";
+  }
+  return "unknown status";
+}
+
+moe_status moe_ctx_create(int device, void *side_stream, moe_ctx **out) {
+  if (!out) return MOE_ERR_INVALID_ARG;
+  *out = nullptr;
+  int n = 0;
+  if (hipGetDeviceCount(&n) != hipSuccess || device < 0 || device >= n) return MOE_ERR_DEVICE;
+  hipDeviceProp_t prop;
+  if (hipGetDeviceProperties(&prop, device) != hipSuccess) return MOE_ERR_DEVICE;
+  if (strncmp(prop.gcnArchName, "gfx950", 6) != 0) return MOE_ERR_DEVICE;
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_DEVICE;
+  if (cur != device && hipSetDevice(device) != hipSuccess) return MOE_ERR_DEVICE;
+  moe_ctx *c = new (std::nothrow) moe_ctx;
+  if (!c) return MOE_ERR_DEVICE;
+  memset(c, 0, sizeof *c);
+  c->device = device;
+  c->side = (hipStream_t)side_stream;
+  hipError_t e1 = hipEventCreateWithFlags(&c->ev_ready, hipEventDisableTiming);
+  hipError_t e2 = hipEventCreateWithFlags(&c->ev_done, hipEventDisableTiming);
+  if (cur != device) (void)hipSetDevice(cur);
+  if (e1 != hipSuccess || e2 != hipSuccess) {
+    if (e1 == hipSuccess) (void)hipEventDestroy(c->ev_ready);
+    if (e2 == hipSuccess) (void)hipEventDestroy(c->ev_done);
+    delete c;
+    return MOE_ERR_DEVICE;
+  }
+  *out = c;
+  return MOE_OK;
+}
+
+moe_status moe_ctx_destroy(moe_ctx *ctx) {
+  if (!ctx) return MOE_ERR_INVALID_ARG;
+  (void)hipEventDestroy(ctx->ev_ready);
+  (void)hipEventDestroy(ctx->ev_done);
+  delete ctx;
+  return MOE_OK;
+}
+
+const char *moe_ctx_last_error(const moe_ctx *ctx) { return ctx ? ctx->last_error : ""; }
+
+size_t moe_workspace_bytes(const moe_desc *desc, int32_t T, int which) {
+  if (check_desc(desc) != MOE_OK || T < 0 || which < MOE_WS_ROUTE || which > MOE_WS_LAYER) return 0;
+  return layout(desc, T, which).total;
+}
+
+size_t moe_packed_bytes(const moe_desc *desc, int shared, int which) {
+  if (check_desc(desc) != MOE_OK || (shared != 0 && shared != 1)) return 0;
+  const size_t E = shared ? 1 : desc->num_experts, H = desc->hidden;
+  const size_t I = shared ? desc->shared_inter : desc->inter;
+  const size_t eb = elem_bytes(desc->expert_dtype);
+  const bool mx = desc->expert_dtype == MOE_MXFP8;
+  switch (which) {
+    case MOE_PACK_GATE_UP: return E * 2 * I * H * eb;
+    case MOE_PACK_DOWN: return E * H * I * eb;
+    case MOE_PACK_GATE_UP_SCALE: return mx ? E * 2 * I * H / 32 : 0;
+    case MOE_PACK_DOWN_SCALE: return mx ? E * H * I / 32 : 0;
+  }
+  return 0;
+}
+
+moe_status moe_pack_experts(const moe_desc *desc, int shared, int src_dtype, const void *gate,
+                            const void *up, const void *down, void *gate_up_out, void *down_out,
+                            uint8_t *gate_up_scale_out, uint8_t *down_scale_out, void *stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  const int E = shared ? 1 : desc->num_experts, H = desc->hidden;
+  const int I = shared ? desc->shared_inter : desc->inter;
+  if (I == 0) return MOE_OK;
+  const bool mx = desc->expert_dtype == MOE_MXFP8;
+  if (!gate || !up || !down || !gate_up_out || !down_out) return MOE_ERR_INVALID_ARG;
+  if (mx && (!gate_up_scale_out || !down_scale_out)) return MOE_ERR_INVALID_ARG;
+  const int F = fmt_of(desc->expert_dtype);
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t err = launch_pack(gate, up, src_dtype == MOE_BF16, E, 2 * I, H, 1, F,
+                               (uint8_t *)gate_up_out, (uint16_t *)gate_up_scale_out, s);
+  if (err == hipSuccess)
+    err = launch_pack(down, nullptr, src_dtype == MOE_BF16, E, H, I, 0, F, (uint8_t *)down_out,
+                      (uint16_t *)down_scale_out, s);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+moe_status moe_mx_quantize(const void *src, int src_dtype, int64_t rows, int64_t cols, uint8_t *q,
+                           uint8_t *scale, void *stream) {
+  if (rows < 0 || cols <= 0 || cols % 32) return MOE_ERR_INVALID_ARG;
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!src || !q || !scale) return MOE_ERR_INVALID_ARG;
+  hipError_t err = launch_mx_quantize(src, src_dtype == MOE_BF16, rows, cols, q, scale,
+                                      (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+moe_status moe_route(moe_ctx *ctx, const moe_desc *desc, const void *x, int32_t T,
+                     const float *router_w, const float *router_bias, int32_t *topk_idx,
+                     float *topk_w, void *ws, size_t ws_bytes, void *stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_ctx(ctx)) != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !router_w || !topk_idx || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  Layout L = layout(desc, T, MOE_WS_ROUTE);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipError_t err = launch_route(x, desc->act_dtype == MOE_BF16, router_w, router_bias,
+                                (float *)((char *)ws + L.logits), topk_idx, topk_w, T,
+                                desc->hidden, desc->num_experts, desc->top_k,
+                                desc->router_scaling_factor, desc->route_norm, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : device_error(ctx, err, "moe_route");
+}
+
+moe_status moe_permute(moe_ctx *ctx, const moe_desc *desc, const int32_t *topk_idx, int32_t T,
+                       int32_t *expert_counts, int32_t *expert_offsets, int32_t *sorted_src,
+                       int32_t *dest, void *ws, size_t ws_bytes, void *stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_ctx(ctx)) != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!topk_idx || !expert_counts || !expert_offsets || !sorted_src || !dest || !ws)
+    return MOE_ERR_INVALID_ARG;
+  Layout L = layout(desc, T, MOE_WS_PERMUTE);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipError_t err = launch_permute(topk_idx, T, desc->num_experts, desc->top_k, expert_counts,
+                                  expert_offsets, sorted_src, dest, (char *)ws + L.perm,
+                                  (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : device_error(ctx, err, "moe_permute");
+}
+
+moe_status moe_grouped_ffn(moe_ctx *ctx, const moe_desc *desc, const moe_weights *w, int shared,
+                           const void *x, int32_t T, const int32_t *sorted_src,
+                           const int32_t *expert_offsets, void *y, void *ws, size_t ws_bytes,
+                           void *stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_ctx(ctx)) != MOE_OK) return st;
+  if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0 || (shared && desc->shared_inter == 0)) return MOE_OK;
+  if (!x || !y || !ws || !weights_ok(desc, w, 0, !shared, shared)) return MOE_ERR_INVALID_ARG;
+  if (!shared && (!sorted_src || !expert_offsets)) return MOE_ERR_INVALID_ARG;
+  Layout L = layout(desc, T, shared ? MOE_WS_SHARED_FFN : MOE_WS_GROUPED_FFN);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char *base = (char *)ws;
+  const bool mx = desc->expert_dtype == MOE_MXFP8;
+  const void *xa = x;
+  const uint8_t *xs = nullptr;
+  hipError_t err = hipSuccess;
+  if (mx) {
+    err = launch_mx_quantize(x, 1, T, desc->hidden, (uint8_t *)base + L.xq,
+                             (uint8_t *)base + L.xs, s);
+    if (err != hipSuccess) return device_error(ctx, err, "moe_grouped_ffn");
+    xa = base + L.xq;
+    xs = (const uint8_t *)base + L.xs;
+  }
+  err = ffn(desc, w, shared, xa, xs, T, sorted_src, expert_offsets, y,
+            base + (shared ? L.sh_h : L.h),
+            mx ? (uint8_t *)base + (shared ? L.sh_hs : L.hs) : nullptr, s);
+  return err == hipSuccess ? MOE_OK : device_error(ctx, err, "moe_grouped_ffn");
+}
+
+moe_status moe_combine(moe_ctx *ctx, const moe_desc *desc, const void *y, const int32_t *dest,
+                       const float *topk_w, const void *shared_out, int32_t T, void *out,
+                       void *stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_ctx(ctx)) != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!y || !dest || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  const int of = fmt_of(desc->out_dtype);
+  hipError_t err = launch_combine(y, of, dest, topk_w, shared_out, T, desc->hidden, desc->top_k,
+                                  out, of, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : device_error(ctx, err, "moe_combine");
+}
+
+moe_status moe_layer_ws_topk(const moe_desc *desc, int32_t T, size_t *idx_offset,
+                             size_t *w_offset) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if (T < 0 || !idx_offset || !w_offset) return MOE_ERR_INVALID_ARG;
+  Layout L = layout(desc, T, MOE_WS_LAYER);
+  *idx_offset = L.idx;
+  *w_offset = L.w;
+  return MOE_OK;
+}
+
+moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weights *w,
+                             const void *x, int32_t T, void *out, void *ws, size_t ws_bytes,
+                             void *stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_ctx(ctx)) != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (T == 0) return MOE_OK;
+  if (!x || !out || !ws || !weights_ok(desc, w, 1, 1, 1)) return MOE_ERR_INVALID_ARG;
+  Layout L = layout(desc, T, MOE_WS_LAYER);
+  if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
+  hipStream_t s = (hipStream_t)stream;
+  char *b = (char *)ws;
+  const int H = desc->hidden, E = desc->num_experts, k = desc->top_k;
+  const bool mx = desc->expert_dtype == MOE_MXFP8;
+  const bool has_shared = desc->shared_inter > 0;
+  int32_t *idx = (int32_t *)(b + L.idx);
+  float *tw = (float *)(b + L.w);
+  int32_t *offsets = (int32_t *)(b + L.offsets);
+  int32_t *src = (int32_t *)(b + L.src);
+  int32_t *dest = (int32_t *)(b + L.dest);
+  hipError_t err;
+#define MOE_TRY(call, where)                          \
+  do {                                                \
+    err = (call);                                     \
+    if (err != hipSuccess) return device_error(ctx, err, where); \
+  } while (0)
+
+  // Gating on the main stream.
+  MOE_TRY(launch_route(x, desc->act_dtype == MOE_BF16, w->router_w, w->router_bias,
+                       (float *)(b + L.logits), idx, tw, T, H, E, k, desc->router_scaling_factor,
+                       desc->route_norm, s),
+          "gating");
+  const void *xa = x;
+  const uint8_t *xs = nullptr;
+  if (mx) {
+    MOE_TRY(launch_mx_quantize(x, 1, T, H, (uint8_t *)b + L.xq, (uint8_t *)b + L.xs, s),
+            "activation quantisation");
+    xa = b + L.xq;
+    xs = (const uint8_t *)b + L.xs;
+  }
+  // Shared expert: on the side stream once the main stream is past gating.
+  const bool two = has_shared && ctx->side && ctx->side != s;
+  if (has_shared) {
+    hipStream_t ss = two ? ctx->side : s;
+    if (two) {
+      MOE_TRY(hipEventRecord(ctx->ev_ready, s), "input-ready event");
+      MOE_TRY(hipStreamWaitEvent(ss, ctx->ev_ready, 0), "side stream wait");
+    }
+    MOE_TRY(ffn(desc, w, 1, xa, xs, T, nullptr, nullptr, b + L.z, b + L.sh_h,
+                mx ? (uint8_t *)b + L.sh_hs : nullptr, ss),
+            "shared expert");
+    if (two) MOE_TRY(hipEventRecord(ctx->ev_done, ss), "shared-done event");
+  }
+  // Routed path on the main stream: InitRouting, grouped GEMM.
+  MOE_TRY(launch_permute(idx, T, E, k, (int32_t *)(b + L.counts), offsets, src, dest, b + L.perm,
+                         s),
+          "permutation");
+  MOE_TRY(ffn(desc, w, 0, xa, xs, T, src, offsets, b + L.y, b + L.h,
+              mx ? (uint8_t *)b + L.hs : nullptr, s),
+          "routed experts");
+  // Join, then FinalizeRouting + shared add.
+  if (two) MOE_TRY(hipStreamWaitEvent(s, ctx->ev_done, 0), "main stream wait");
+  const int of = fmt_of(desc->out_dtype);
+  MOE_TRY(launch_combine(b + L.y, of, dest, tw, has_shared ? b + L.z : nullptr, T, H, k, out, of, s),
+          "combine");
+#undef MOE_TRY
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,146 @@
+// moe_common.hpp -- device helpers shared by the MoE layer kernels (gfx950).
+//
+// Fragment layout used by every matrix kernel.  A "chunk" is 256 bytes of
+// one row along the reduction axis K (128 bf16, 256 fp8 or 64 fp32
+// elements), split into two 128-byte halves.  A block of 16 rows x 1 chunk
+// is held by one wave: lane l owns row l % 16 and, with lane group
+// g = l / 16, four 16-byte pieces p = 0..3 at chunk byte offset
+//     off(g, p) = 128 * (p / 2) + 64 * (p % 2) + 16 * g,
+// i.e. in half h the row's bytes [0, 64) are piece 2h of lane groups 0-3 and
+// bytes [64, 128) are piece 2h+1.  A half-chunk stage therefore reads one
+// contiguous 128-byte line of every row.  Packed weight blocks and LDS tiles
+// store a block as [piece][lane][16 bytes] (4 KiB, or 2 KiB per half), so
+// one wave-wide 16-byte access touches a contiguous 1 KiB.
+//
+// Matrix-core steps: bf16 v_mfma_f32_16x16x32_bf16 contracts one piece (8
+// elements per lane), 2 per half-chunk; fp32 v_mfma_f32_16x16x4f32 one
+// element, 8 per half-chunk; MX-fp8 v_mfma_scale_f32_16x16x128_f8f6f4 both
+// pieces of a half (32 bytes per lane), 1 per half-chunk.  The weight and
+// the token operand use the same (lane group, piece, element) -> k
+// assignment, so every step contracts matching k on both sides.
+//
+// MX scales.  On gfx950 the scaled 16x16x128 instruction treats byte i of
+// lane group g's 32 operand bytes as K index 64 * (i / 16) + 16 * g + i % 16,
+// and takes the scale of K block b (K in [32b, 32b + 32)) from lane group b
+// (measured on the device).  With the piece offsets above, K block b of half
+// h is exactly the 32-element MX block 4h + b of the chunk (row bytes
+// [32b, 32b + 32) of the half), so lane group g supplies the E8M0 scale of
+// MX block 4h + g while its data bytes belong to blocks g/2 and 2 + g/2.
+//
+// The weights are the MFMA A operand (16 output features) and the tokens
+// the B operand (16 tokens), so the 16x16 accumulator of lane l holds
+// token m = l % 16 and output features n = 4 * (l / 16) + r, r = 0..3.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kChunkBytes = 256;      // bytes of one row per K chunk
+constexpr int kBlockBytes = 4096;     // 16 rows x 1 chunk
+constexpr int kLaneBytes = 64;        // one lane's share of a block
+
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(8))) int i32x8;
+typedef __attribute__((ext_vector_type(4))) int i32x4;
+
+enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MX8 = 2 };
+
+template <int F> struct FmtInfo;
+template <> struct FmtInfo<FMT_F32> { static constexpr int elem_bytes = 4, chunk_elems = 64; };
+template <> struct FmtInfo<FMT_BF16> { static constexpr int elem_bytes = 2, chunk_elems = 128; };
+template <> struct FmtInfo<FMT_MX8> { static constexpr int elem_bytes = 1, chunk_elems = 256; };
+
+// ----------------------------------------------------------------------------- conversions
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// OCP MX E4M3 (FN) rounding of a finite fp32 value: round to nearest even,
+// saturate to +-448, keep the sign (also for results that round to zero).
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+  uint32_t sign = (__float_as_uint(v) >> 24) & 0x80u;
+  float a = fabsf(v);
+  if (a >= 448.0f) return sign | 0x7Eu;
+  if (a < 0.015625f) {                         // below 2^-6: multiples of 2^-9
+    return sign | (uint32_t)rintf(a * 512.0f);  // 8 becomes the smallest normal
+  }
+  uint32_t bits = __float_as_uint(a);
+  int e = (int)((bits >> 23) & 0xFFu) - 127;
+  uint32_t man = bits & 0x7FFFFFu;
+  uint32_t q = man >> 20, rem = man & 0xFFFFFu;
+  if (rem > 0x80000u || (rem == 0x80000u && (q & 1u))) ++q;
+  if (q == 8u) { q = 0u; ++e; }
+  if (e > 8 || (e == 8 && q == 7u)) return sign | 0x7Eu;
+  return sign | ((uint32_t)(e + 7) << 3) | q;
+}
+
+// Shared exponent X of an MX block from its largest magnitude (exact):
+// X = floor(log2 amax) - 8, clamped below at -127 (zero and fp32-subnormal
+// maxima give -127).  Returned as the E8M0 byte X + 127.
+__device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
+  int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);   // 0 for zero/subnormal
+  int X = ef - 127 - 8;
+  if (ef == 0 || X < -127) X = -127;
+  return (uint32_t)(X + 127);
+}
+
+// 2^-X as an fp32 for an E8M0 byte s = X + 127 (X in [-127, 119]).
+__device__ __forceinline__ float mx_inv_scale(uint32_t s) {
+  return __uint_as_float((uint32_t)(254 - (int)s) << 23);
+}
+
+// ----------------------------------------------------------------------------- wave helpers
+
+__device__ __forceinline__ float wave_max_xor(float v, int mask) {
+  return fmaxf(v, __shfl_xor(v, mask, 64));
+}
+
+// ----------------------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ int chunk_off(int g, int p) { return 128 * (p >> 1) + 64 * (p & 1) + 16 * g; }
+
+// acc += W x T over one half-chunk.  w, t: the lane's two 16-byte pieces of
+// this half.  ws, ts: E8M0 scale bytes of the lane's MX block in bits 7:0
+// (MX only; opsel 0 selects them).
+template <int F>
+__device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32x4 &w1,
+                                          const i32x4 &t0, const i32x4 &t1, uint32_t ws,
+                                          uint32_t ts) {
+  if constexpr (F == FMT_BF16) {
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w0),
+                                                  __builtin_bit_cast(bf16x8, t0), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, w1),
+                                                  __builtin_bit_cast(bf16x8, t1), acc, 0, 0, 0);
+  } else if constexpr (F == FMT_F32) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(w0[e]), __int_as_float(t0[e]), acc,
+                                                 0, 0, 0);
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(w1[e]), __int_as_float(t1[e]), acc,
+                                                 0, 0, 0);
+  } else {
+    i32x8 a = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    i32x8 b = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    // operand format 0 = fp8 E4M3 for A and B; opsel 0 = scale byte 0
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, (int)ws, 0, (int)ts);
+  }
+}
+
+__device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
+  // Workgroups are dispatched round-robin over the 8 XCDs.  Give each XCD a
+  // contiguous range of logical tiles so neighbouring tiles (which share
+  // weights) meet in the same L2.  nblocks must be a multiple of 8.
+  int per = nblocks >> 3;
+  return (bid & 7) * per + (bid >> 3);
+}
+
+}  // namespace moe

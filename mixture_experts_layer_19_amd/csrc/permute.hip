@@ -1,0 +1,138 @@
+// permute.hip -- InitRouting: group the (token, slot) pairs by expert.
+//
+// Hy3 on CANN NPU guide, section 8.1 (MoE EP) and section 8.5: InitRouting
+// matches tokens to experts ahead of the grouped GEMM.  Pair f = t*k + j goes
+// to row r = offsets[e] + #{earlier pairs routed to e}, so each expert's rows
+// are in ascending token order.  Because a token's k experts are distinct,
+// that rank is the number of earlier *tokens* that picked e, which is what
+// the kernels count: per block of 256 tokens a bitmap column per expert
+// (bit t set when token t picked e), block totals scanned per expert, and a
+// popcount of the bits below t.  Everything is integer and order-free, so the
+// result is deterministic and exactly the stable order.
+#include "moe_common.hpp"
+#include "moe_launch.hpp"
+
+namespace moe {
+
+constexpr int kPermBlock = 256;               // tokens per block
+constexpr int kPermWords = kPermBlock / 32;   // bitmap words per (block, expert)
+
+// Phase 1: per token block, the bitmap column of every expert and its count.
+__global__ __launch_bounds__(256) void perm_count_kernel(const int32_t *__restrict__ topk_idx, int T,
+                                                         int E, int k, uint32_t *__restrict__ bits,
+                                                         int32_t *__restrict__ blk_count) {
+  extern __shared__ uint32_t col[];           // [E][kPermWords]
+  const int b = blockIdx.x, tid = threadIdx.x;
+  for (int i = tid; i < E * kPermWords; i += 256) col[i] = 0u;
+  __syncthreads();
+  const int t = b * kPermBlock + tid;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      int e = topk_idx[(size_t)t * k + j];
+      if (e >= 0 && e < E) atomicOr(&col[e * kPermWords + (tid >> 5)], 1u << (tid & 31));
+    }
+  }
+  __syncthreads();
+  uint32_t *out = bits + (size_t)b * E * kPermWords;
+  for (int i = tid; i < E * kPermWords; i += 256) out[i] = col[i];
+  for (int e = tid; e < E; e += 256) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kPermWords; ++w) c += __popc(col[e * kPermWords + w]);
+    blk_count[(size_t)b * E + e] = c;
+  }
+}
+
+// Phase 2 (one workgroup): per-expert exclusive scan over blocks, the
+// per-expert counts, and the exclusive scan over experts.
+__global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restrict__ blk_count,
+                                                         int nblk, int E,
+                                                         int32_t *__restrict__ blk_base,
+                                                         int32_t *__restrict__ counts,
+                                                         int32_t *__restrict__ offsets) {
+  __shared__ int32_t tot[1024];
+  const int tid = threadIdx.x;
+  // blockDim.x == 256: each thread owns entries tid + 256 i, i < 4.
+  for (int e = tid; e < 1024; e += blockDim.x) tot[e] = 0;
+  __syncthreads();
+  for (int e = tid; e < E; e += blockDim.x) {
+    int run = 0;
+    for (int b = 0; b < nblk; ++b) {
+      blk_base[(size_t)b * E + e] = run;
+      run += blk_count[(size_t)b * E + e];
+    }
+    counts[e] = run;
+    tot[e] = run;
+  }
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 1024 entries (E <= 1024).
+  for (int d = 1; d < 1024; d <<= 1) {
+    int v[4];
+    int n = 0;
+    for (int e = tid; e < 1024; e += blockDim.x) v[n++] = (e >= d) ? tot[e - d] : 0;
+    __syncthreads();
+    n = 0;
+    for (int e = tid; e < 1024; e += blockDim.x) tot[e] += v[n++];
+    __syncthreads();
+  }
+  for (int e = tid; e <= E; e += blockDim.x) offsets[e] = (e == 0) ? 0 : tot[e - 1];
+}
+
+// Phase 3: every pair computes its row and writes both directions.
+__global__ __launch_bounds__(256) void perm_scatter_kernel(
+    const int32_t *__restrict__ topk_idx, int T, int E, int k, const uint32_t *__restrict__ bits,
+    const int32_t *__restrict__ blk_base, const int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_src, int32_t *__restrict__ dest) {
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const int t = b * kPermBlock + tid;
+  if (t >= T) return;
+  const int word = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+  for (int j = 0; j < k; ++j) {
+    const int f = t * k + j;
+    const int e = topk_idx[f];
+    if (e < 0 || e >= E) continue;
+    const uint32_t *c = bits + ((size_t)b * E + e) * kPermWords;
+    int rank = __popc(c[word] & below);
+    for (int w = 0; w < word; ++w) rank += __popc(c[w]);
+    const int r = offsets[e] + blk_base[(size_t)b * E + e] + rank;
+    sorted_src[r] = f;
+    dest[f] = r;
+  }
+}
+
+size_t permute_ws_bytes(int T, int E) {
+  size_t nblk = (size_t)(T + kPermBlock - 1) / kPermBlock;
+  size_t b = nblk * E * kPermWords * sizeof(uint32_t);
+  b = (b + 255) & ~(size_t)255;
+  size_t c = nblk * E * sizeof(int32_t);
+  c = (c + 255) & ~(size_t)255;
+  return b + 2 * c;
+}
+
+hipError_t launch_permute(const int32_t *topk_idx, int T, int E, int k, int32_t *counts,
+                          int32_t *offsets, int32_t *sorted_src, int32_t *dest, void *ws,
+                          hipStream_t stream) {
+  const int nblk = (T + kPermBlock - 1) / kPermBlock;
+  size_t nb = (size_t)nblk * E * kPermWords * sizeof(uint32_t);
+  nb = (nb + 255) & ~(size_t)255;
+  size_t nc = (size_t)nblk * E * sizeof(int32_t);
+  nc = (nc + 255) & ~(size_t)255;
+  uint32_t *bits = (uint32_t *)ws;
+  int32_t *blk_count = (int32_t *)((char *)ws + nb);
+  int32_t *blk_base = (int32_t *)((char *)ws + nb + nc);
+  if (nblk > 0) {
+    perm_count_kernel<<<nblk, 256, (size_t)E * kPermWords * sizeof(uint32_t), stream>>>(
+        topk_idx, T, E, k, bits, blk_count);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  perm_scan_kernel<<<1, 256, 0, stream>>>(blk_count, nblk, E, blk_base, counts, offsets);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || nblk == 0) return err;
+  perm_scatter_kernel<<<nblk, 256, 0, stream>>>(topk_idx, T, E, k, bits, blk_base, offsets,
+                                                sorted_src, dest);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -317,43 +317,43 @@ ORC_EXPORT int oracle_swiglu_rows(int64_t M, int64_t H, int64_t I, const float *
     g_src = wg_q; u_src = wu_q; d_src = wd_q;
   }
 
+  /* Rows one after another; inside a row every output element is one
+   * thread's fixed-order sum, so results do not depend on the thread count. */
   int rc = 0;
-#pragma omp parallel
-  {
-    float *xt = (float *)malloc(sizeof(float) * (size_t)H);
-    float *hr = (float *)malloc(sizeof(float) * (size_t)I);
-    float *ht = (float *)malloc(sizeof(float) * (size_t)I);
-    if (!xt || !hr || !ht) {
-#pragma omp atomic write
-      rc = -1;
-    } else {
-#pragma omp for schedule(static)
-      for (int64_t m = 0; m < M; ++m) {
-        if (mx) mx_roundtrip_row(H, xr + m * H, xt);
-        else memcpy(xt, xr + m * H, sizeof(float) * (size_t)H);
-        for (int64_t i = 0; i < I; ++i) {
-          double g = 0.0, u = 0.0;
-          for (int64_t h = 0; h < H; ++h) {
-            g += (double)xt[h] * load_w(g_src, mx ? 0 : wdtype, i * H + h);
-            u += (double)xt[h] * load_w(u_src, mx ? 0 : wdtype, i * H + h);
-          }
-          double silu = g / (1.0 + exp(-g));
-          hr[i] = (float)(silu * u);
+  float *xt = (float *)malloc(sizeof(float) * (size_t)H);
+  float *hr = (float *)malloc(sizeof(float) * (size_t)I);
+  float *ht = (float *)malloc(sizeof(float) * (size_t)I);
+  if (!xt || !hr || !ht) {
+    rc = -1;
+  } else {
+    const int gdt = mx ? 0 : wdtype;
+    for (int64_t m = 0; m < M; ++m) {
+      if (mx) mx_roundtrip_row(H, xr + m * H, xt);
+      else memcpy(xt, xr + m * H, sizeof(float) * (size_t)H);
+#pragma omp parallel for schedule(static)
+      for (int64_t i = 0; i < I; ++i) {
+        double g = 0.0, u = 0.0;
+        for (int64_t h = 0; h < H; ++h) {
+          g += (double)xt[h] * load_w(g_src, gdt, i * H + h);
+          u += (double)xt[h] * load_w(u_src, gdt, i * H + h);
         }
-        if (h_out) memcpy(h_out + m * I, hr, sizeof(float) * (size_t)I);
-        if (mx) mx_roundtrip_row(I, hr, ht);
-        else memcpy(ht, hr, sizeof(float) * (size_t)I);
-        for (int64_t n = 0; n < H; ++n) {
-          double acc = 0.0;
-          for (int64_t i = 0; i < I; ++i) acc += (double)ht[i] * load_w(d_src, mx ? 0 : wdtype, n * I + i);
-          y[m * H + n] = (float)acc;
-        }
+        double silu = g / (1.0 + exp(-g));
+        hr[i] = (float)(silu * u);
+      }
+      if (h_out) memcpy(h_out + m * I, hr, sizeof(float) * (size_t)I);
+      if (mx) mx_roundtrip_row(I, hr, ht);
+      else memcpy(ht, hr, sizeof(float) * (size_t)I);
+#pragma omp parallel for schedule(static)
+      for (int64_t n = 0; n < H; ++n) {
+        double acc = 0.0;
+        for (int64_t i = 0; i < I; ++i) acc += (double)ht[i] * load_w(d_src, gdt, n * I + i);
+        y[m * H + n] = (float)acc;
       }
     }
-    free(xt);
-    free(hr);
-    free(ht);
   }
+  free(xt);
+  free(hr);
+  free(ht);
   free(wg_q);
   free(wu_q);
   free(wd_q);

@@ -1,0 +1,90 @@
+"""Shared helpers for the GPU parity tests (not collected by pytest)."""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+from mixture_experts_layer_19_amd import inputs as I
+
+TIE_MARGIN = 1e-6          # sigmoid-score margin inside which a routing flip is a tie
+TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 3e-2}
+
+_layers = {}
+
+
+def device_layer(w: I.Workload):
+    """One DeviceLayer per distinct weight set (decode and prefill share)."""
+    from mixture_experts_layer_19_amd.layer import DeviceLayer
+    key = (w.H, w.E, w.k, w.I, w.Is, w.dtype, w.seed, w.zipf_beta)
+    if key not in _layers:
+        print("[gpu] building layer %s" % (key,), flush=True)
+        _layers[key] = DeviceLayer(w)
+    lay = _layers[key]
+    lay.w = w
+    return lay
+
+
+def to_numpy(t):
+    import torch
+    t = t.detach()
+    if t.dtype == torch.bfloat16:
+        return t.float().cpu().numpy()
+    return t.cpu().numpy()
+
+
+def rel_max_err(gpu, ref):
+    gpu = np.asarray(gpu, np.float64)
+    ref = np.asarray(ref, np.float64)
+    return float(np.abs(gpu - ref).max() / np.abs(ref).max())
+
+
+def classify_routing(g_idx, o_idx, scores):
+    """Rows where the GPU's indices differ from the oracle's.  A row is a tie
+    flip when, slot by slot, the oracle's scores of the two experts differ by
+    at most TIE_MARGIN (a swap at the top-k boundary or inside the selection
+    among near-equal scores).  Returns (mismatch mask, tie-flip mask)."""
+    mism = (g_idx != o_idx).any(axis=1)
+    flips = np.zeros_like(mism)
+    for t in np.nonzero(mism)[0]:
+        sg = scores[t, g_idx[t]].astype(np.float64)
+        so = scores[t, o_idx[t]].astype(np.float64)
+        distinct = len(set(g_idx[t].tolist())) == len(g_idx[t])
+        in_range = np.all((g_idx[t] >= 0) & (g_idx[t] < scores.shape[1]))
+        flips[t] = distinct and in_range and np.all(np.abs(sg - so) <= TIE_MARGIN)
+    return mism, flips
+
+
+def expert_weights_parallel(w: I.Workload, experts, threads=None):
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+    experts = sorted(set(int(e) for e in experts))
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        vals = list(ex.map(lambda e: I.expert_stored(w, e), experts))
+    return dict(zip(experts, vals))
+
+
+def unpack_blocks(packed: np.ndarray, E: int, N: int, row_bytes: int) -> np.ndarray:
+    """Inverse of the packed fragment layout: bytes [E, N/16, K/256, piece 4,
+    lane 64, 16] -> dense bytes [E, N, row_bytes], with lane l = row l % 16,
+    lane group g = l / 16, and piece p at chunk byte 128 (p/2) + 64 (p%2) + 16 g."""
+    nb, kc = N // 16, row_bytes // 256
+    a = packed.reshape(E, nb, kc, 2, 2, 4, 16, 16)       # e nb kc ph pl g r byte
+    a = a.transpose(0, 1, 6, 2, 3, 4, 5, 7)               # e nb r kc ph pl g byte
+    return a.reshape(E, N, row_bytes)
+
+
+def unpack_scales(packed: np.ndarray, E: int, N: int, K: int) -> np.ndarray:
+    """Packed uint16 scale pairs [E, N/16, K/256, lane] -> E8M0 bytes [E, N, K/32].
+    Byte h of lane l is the scale of 32-block 8 kc + 4 h + l / 16 of row l % 16."""
+    nb, kc = N // 16, K // 256
+    b = packed.view(np.uint8).reshape(E, nb, kc, 4, 16, 2)   # e nb kc g r h
+    b = b.transpose(0, 1, 4, 2, 5, 3)                         # e nb r kc h g
+    return b.reshape(E, N, K // 32)
+
+
+def virtual_to_gate_up(dense: np.ndarray, I_: int):
+    """Split interleaved gate/up virtual rows (16-row blocks alternate)."""
+    E = dense.shape[0]
+    a = dense.reshape(E, I_ // 16, 2, 16, -1)
+    return a[:, :, 0].reshape(E, I_, -1), a[:, :, 1].reshape(E, I_, -1)

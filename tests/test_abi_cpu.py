@@ -1,0 +1,110 @@
+"""Host-side checks of the C-ABI library (no GPU needed): it builds, loads, and
+exports every entry point include/moe.h declares; host-only calls validate
+their arguments."""
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^MOE_API\s+[\w\s\*]+?\b(moe_\w+)\s*\(", src, re.M)))
+
+
+@pytest.fixture(scope="module")
+def B():
+    from mixture_experts_layer_19_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        from mixture_experts_layer_19_amd import build
+        build.build()
+    binding.lib()
+    return binding
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ("moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    lib = B.lib()
+    for n in _declared():
+        assert hasattr(lib, n), n
+    assert sorted(B.EXPORTS) == _declared()
+
+
+def test_exports_are_c_symbols(B):
+    out = os.popen("nm -D --defined-only %s" % B.LIB_PATH).read()
+    syms = set(l.split()[-1] for l in out.splitlines() if l.strip())
+    for n in _declared():
+        assert n in syms, n
+
+
+def test_status_strings(B):
+    for s in range(5):
+        assert B.moe_status_string(s)
+    assert B.moe_status_string(99) == "unknown status"
+
+
+def _desc(B, **kw):
+    d = dict(hidden=4096, num_experts=192, top_k=8, inter=1536, shared_inter=1536,
+             router_scaling_factor=2.826, route_norm=1, act_dtype=B.MOE_BF16,
+             expert_dtype=B.MOE_BF16, out_dtype=B.MOE_BF16)
+    d.update(kw)
+    return B.MoeDesc(**d)
+
+
+def test_workspace_and_packed_sizes(B):
+    d = _desc(B)
+    assert B.moe_packed_bytes(d, 0, B.MOE_PACK_GATE_UP) == 192 * 2 * 1536 * 4096 * 2
+    assert B.moe_packed_bytes(d, 0, B.MOE_PACK_DOWN) == 192 * 4096 * 1536 * 2
+    assert B.moe_packed_bytes(d, 1, B.MOE_PACK_GATE_UP) == 2 * 1536 * 4096 * 2
+    assert B.moe_packed_bytes(d, 0, B.MOE_PACK_GATE_UP_SCALE) == 0
+    mx = _desc(B, expert_dtype=B.MOE_MXFP8)
+    assert B.moe_packed_bytes(mx, 0, B.MOE_PACK_GATE_UP) == 192 * 2 * 1536 * 4096
+    assert B.moe_packed_bytes(mx, 0, B.MOE_PACK_DOWN_SCALE) == 192 * 4096 * 1536 // 32
+    ws = B.moe_workspace_bytes(d, 64, B.MOE_WS_LAYER)
+    # holds at least y [T*k, H] bf16 and the shared output [T, H]
+    assert ws >= 64 * 8 * 4096 * 2 + 64 * 4096 * 2
+    assert B.moe_workspace_bytes(d, 0, B.MOE_WS_LAYER) >= 0
+    assert B.moe_workspace_bytes(d, -1, B.MOE_WS_LAYER) == 0
+    assert B.moe_workspace_bytes(d, 64, 17) == 0
+    i0, w0 = B.moe_layer_ws_topk(d, 64)
+    assert i0 != w0
+
+
+@pytest.mark.parametrize("bad", [dict(top_k=0), dict(top_k=17), dict(num_experts=2000),
+                                 dict(top_k=9, num_experts=8), dict(hidden=100),
+                                 dict(inter=100), dict(route_norm=3), dict(act_dtype=7)])
+def test_bad_descriptors_are_rejected(B, bad):
+    d = _desc(B, **bad)
+    assert B.moe_workspace_bytes(d, 64, B.MOE_WS_LAYER) == 0
+    assert B.moe_packed_bytes(d, 0, B.MOE_PACK_GATE_UP) == 0
+
+
+def test_unsupported_dtype_combination(B):
+    d = _desc(B, act_dtype=B.MOE_F32)            # fp32 x with bf16 experts
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_pack_experts(d, 0, B.MOE_BF16, 1, 1, 1, 1, 1)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+
+
+def test_mx_quantize_argument_checks(B):
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_mx_quantize(1, B.MOE_F32, 4, 33, 1, 1)       # cols not a multiple of 32
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoeError):
+        B.moe_mx_quantize(None, B.MOE_F32, 4, 32, 1, 1)
+    B.moe_mx_quantize(None, B.MOE_F32, 0, 32, None, None)   # zero rows: no-op
+
+
+def test_null_context_is_rejected(B):
+    d = _desc(B)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_route(None, d, 1, 4, 1, None, 1, 1, 1, 1 << 30)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG

@@ -1,0 +1,137 @@
+"""Whole-layer parity: moe_layer_forward (routing, permutation, grouped FFN,
+shared expert on the side stream, combine) against the oracle on the five
+workloads.  The tiny workload is compared on every output; the full-size
+workloads on sampled tokens the oracle evaluates one by one from the
+definition, in the same launch configuration the benchmark times.  Tokens
+whose routing differs from the oracle's only by ties within 1e-6 of the
+sigmoid score are counted, checked to be valid selections, and left out of
+the element-wise comparison."""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+from mixture_experts_layer_19_amd import binding as B
+from mixture_experts_layer_19_amd import inputs as I
+from mixture_experts_layer_19_amd.layer import DeviceLayer, to_device
+
+from _gpu import (TOL, classify_routing, device_layer, expert_weights_parallel, rel_max_err,
+                  to_numpy)
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu_forward(lay, w, T):
+    xg, x = I.x_input(w, T)
+    xd = to_device(xg)
+    out = lay.forward(xd)
+    torch.cuda.synchronize()
+    ws = lay.workspace(T)
+    io, wo = B.moe_layer_ws_topk(lay.desc, T)
+    P = T * w.k
+    g_idx = ws[io:io + 4 * P].view(torch.int32).reshape(T, w.k).cpu().numpy()
+    return x, xd, to_numpy(out), g_idx
+
+
+def _sample_tokens(w, o_idx_all=None, n_rand=16):
+    T = w.T
+    toks = set(range(min(8, T))) | set(range(max(0, T - 8), T))
+    rng = np.random.default_rng(12345)
+    toks |= set(rng.choice(T, size=min(n_rand, T), replace=False).tolist())
+    if o_idx_all is not None:
+        # tokens routed to the busiest expert
+        counts = np.bincount(o_idx_all.ravel(), minlength=w.E)
+        hot = int(np.argmax(counts))
+        hot_toks = np.nonzero((o_idx_all == hot).any(1))[0]
+        toks |= set(hot_toks[:: max(1, len(hot_toks) // 6)][:6].tolist())
+    return np.array(sorted(toks))
+
+
+def _check_layer(orc, name, T=None, full=False):
+    w = I.workload(name) if T is None else I.workload(name, T=T)
+    lay = device_layer(w)
+    x, xd, out, g_idx = _gpu_forward(lay, w, w.T)
+    assert np.isfinite(out).all()
+    Wr, b = I.router_weight(w), I.router_bias(w)
+    o_idx_all, _, scores, _ = orc.route(x, Wr, b, w.k, w.rho, w.route_norm)
+    mism, flips = classify_routing(g_idx, o_idx_all, scores)
+    assert not (mism & ~flips).any()
+    toks = np.arange(w.T) if full else _sample_tokens(w, o_idx_all)
+    keep = toks[~flips[toks]]
+    experts = o_idx_all[keep].ravel()
+    ew = expert_weights_parallel(w, experts)
+    ref, o_idx, _, _ = orc.layer_forward_tokens(
+        keep, x, Wr, b, lambda e: ew[e], I.shared_stored(w), k=w.k, rho=w.rho,
+        route_norm=w.route_norm, mx=(w.dtype == "mxfp8"))
+    np.testing.assert_array_equal(o_idx, o_idx_all[keep])
+    err = rel_max_err(out[keep], ref)
+    print("[layer] %s T=%d: %d tokens compared, %d tie flips, rel err %.3g"
+          % (name, w.T, len(keep), flips.sum(), err))
+    assert err <= TOL[w.dtype], err
+    return out
+
+
+def test_layer_tiny_all_tokens(orc):
+    _check_layer(orc, "tiny", full=True)
+
+
+def test_layer_hy3_decode_all_tokens(orc):
+    _check_layer(orc, "hy3_decode", full=True)
+
+
+def test_layer_hy3_prefill_sampled(orc):
+    _check_layer(orc, "hy3_prefill")
+
+
+def test_layer_hy4_skew_sampled(orc):
+    _check_layer(orc, "hy4_skew")
+
+
+def test_layer_mx_sampled(orc):
+    _check_layer(orc, "mx")
+
+
+@pytest.mark.parametrize("T", [1, 5, 77, 300])
+def test_layer_ragged_token_counts(orc, T):
+    _check_layer(orc, "hy3_decode", T=T, full=T <= 77)
+
+
+def test_layer_zero_tokens_is_a_noop():
+    w = I.workload("tiny")
+    lay = device_layer(w)
+    out = torch.full((1, w.H), 7.0, device="cuda")
+    x = torch.empty((0, w.H), device="cuda")
+    B.moe_layer_forward(lay.ctx, lay.desc, lay.weights, x, 0, out, None, 0)
+    torch.cuda.synchronize()
+    assert torch.all(out == 7.0)
+
+
+@pytest.mark.parametrize("name", ["tiny", "hy3_decode"])
+def test_layer_is_deterministic_and_stream_independent(name):
+    w = I.workload(name)
+    lay = device_layer(w)
+    xg, _ = I.x_input(w)
+    xd = to_device(xg)
+    a = lay.forward(xd).clone()
+    b = lay.forward(xd).clone()
+    # the same layer with the shared expert on the caller's stream
+    ctx1 = B.moe_ctx_create(0, None)
+    c = torch.empty_like(a)
+    ws = lay.workspace(w.T)
+    B.moe_layer_forward(ctx1, lay.desc, lay.weights, xd, w.T, c, ws, ws.numel())
+    torch.cuda.synchronize()
+    B.moe_ctx_destroy(ctx1)
+    assert torch.equal(a, b)
+    assert torch.equal(a, c)
+
+
+def test_layer_workspace_too_small():
+    w = I.workload("tiny")
+    lay = device_layer(w)
+    xg, _ = I.x_input(w)
+    ws = lay.workspace(w.T)
+    out = torch.empty((w.T, w.H), device="cuda")
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_layer_forward(lay.ctx, lay.desc, lay.weights, to_device(xg), w.T, out, ws,
+                            ws.numel() - 1)
+    assert ei.value.status == B.MOE_ERR_WORKSPACE
