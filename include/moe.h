@@ -209,6 +209,23 @@ MOE_API moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc /* host 
                              const moe_weights *w /* host */, const void *x, int32_t T, void *out,
                              void *ws, size_t ws_bytes, void *stream);
 
+/* Per-stage timing of moe_layer_forward.  With profiling enabled the call
+ * records a pair of timing events around each stage on the stream the stage
+ * runs on; moe_ctx_stage_ms then waits for the last call's events and writes
+ * each stage's duration in milliseconds (0 for stages that did not run):
+ *   MOE_STAGE_ROUTE, MOE_STAGE_MX_QUANT, MOE_STAGE_PERMUTE,
+ *   MOE_STAGE_GATE_UP (routed gate/up GEMM + SwiGLU, one kernel),
+ *   MOE_STAGE_DOWN (routed down GEMM, one kernel),
+ *   MOE_STAGE_SHARED_GATE_UP, MOE_STAGE_SHARED_DOWN, MOE_STAGE_COMBINE.
+ * Enabling creates the events (the only allocation after moe_ctx_create);
+ * the timing adds an event record between kernels, so leave it off when the
+ * layer's own latency is what is measured. */
+enum { MOE_STAGE_ROUTE = 0, MOE_STAGE_MX_QUANT = 1, MOE_STAGE_PERMUTE = 2, MOE_STAGE_GATE_UP = 3,
+       MOE_STAGE_DOWN = 4, MOE_STAGE_SHARED_GATE_UP = 5, MOE_STAGE_SHARED_DOWN = 6,
+       MOE_STAGE_COMBINE = 7, MOE_NUM_STAGES = 8 };
+MOE_API moe_status moe_ctx_set_profiling(moe_ctx *ctx, int enable);
+MOE_API moe_status moe_ctx_stage_ms(moe_ctx *ctx, float *ms /* host, MOE_NUM_STAGES */);
+
 /* Byte offsets, inside a moe_layer_forward workspace for T tokens, of the
  * topk_idx [T,k] int32 and topk_w [T,k] fp32 arrays the call wrote. */
 MOE_API moe_status moe_layer_ws_topk(const moe_desc *desc /* host */, int32_t T,

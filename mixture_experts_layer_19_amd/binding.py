@@ -23,7 +23,9 @@ MOE_PACK_GATE_UP, MOE_PACK_DOWN, MOE_PACK_GATE_UP_SCALE, MOE_PACK_DOWN_SCALE = r
 EXPORTS = ("moe_ctx_create", "moe_ctx_destroy", "moe_status_string", "moe_ctx_last_error",
            "moe_workspace_bytes", "moe_packed_bytes", "moe_pack_experts", "moe_mx_quantize",
            "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_ws_topk")
+           "moe_layer_ws_topk", "moe_ctx_set_profiling", "moe_ctx_stage_ms")
+STAGES = ("route", "mx_quant", "permute", "gate_up", "down", "shared_gate_up", "shared_down",
+          "combine")
 
 
 class MoeDesc(ctypes.Structure):
@@ -76,6 +78,8 @@ def lib():
             "moe_combine": ([P, DP, P, P, P, P, I32, P, P], ctypes.c_int),
             "moe_layer_forward": ([P, DP, WP, P, I32, P, P, S, P], ctypes.c_int),
             "moe_layer_ws_topk": ([DP, I32, ctypes.POINTER(S), ctypes.POINTER(S)], ctypes.c_int),
+            "moe_ctx_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
+            "moe_ctx_stage_ms": ([P, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
         }
         for name, (args, res) in sig.items():
             f = getattr(L, name)
@@ -183,3 +187,13 @@ def moe_layer_ws_topk(desc, T):
     a, b = ctypes.c_size_t(), ctypes.c_size_t()
     _check(lib().moe_layer_ws_topk(ctypes.byref(desc), T, ctypes.byref(a), ctypes.byref(b)))
     return a.value, b.value
+
+
+def moe_ctx_set_profiling(ctx, enable: bool):
+    _check(lib().moe_ctx_set_profiling(ctx, int(bool(enable))), ctx)
+
+
+def moe_ctx_stage_ms(ctx) -> dict:
+    arr = (ctypes.c_float * len(STAGES))()
+    _check(lib().moe_ctx_stage_ms(ctx, arr), ctx)
+    return dict(zip(STAGES, (float(v) for v in arr)))

@@ -24,6 +24,9 @@ struct moe_ctx {
   hipEvent_t ev_ready;   // recorded on the caller's stream after gating
   hipEvent_t ev_done;    // recorded on the side stream after the shared expert
   char last_error[256];
+  int profiling;
+  hipEvent_t prof[2 * MOE_NUM_STAGES];   // start/stop per stage (timing events)
+  unsigned ran;                          // stages recorded by the last call
 };
 
 namespace {
@@ -73,7 +76,8 @@ Layout layout(const moe_desc *d, int T, int which) {
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
   const bool layer = which == MOE_WS_LAYER;
-  if (which == MOE_WS_ROUTE || layer) L.logits = take((size_t)T * E * 4);
+  if (which == MOE_WS_ROUTE || layer)
+    L.logits = take(route_ws_bytes(T, (int)H, (int)E, d->act_dtype == MOE_BF16));
   if (layer) {
     L.idx = take(P * 4);
     L.w = take(P * 4);
@@ -110,6 +114,19 @@ moe_status device_error(moe_ctx *ctx, hipError_t err, const char *where) {
   return MOE_ERR_DEVICE;
 }
 
+// Stage timing: record the start/stop event of stage st on stream s.
+struct StageTimer {
+  moe_ctx *c;
+  hipError_t start(int st, hipStream_t s) {
+    if (!c->profiling) return hipSuccess;
+    c->ran |= 1u << st;
+    return hipEventRecord(c->prof[2 * st], s);
+  }
+  hipError_t stop(int st, hipStream_t s) {
+    return c->profiling ? hipEventRecord(c->prof[2 * st + 1], s) : hipSuccess;
+  }
+};
+
 moe_status check_ctx(moe_ctx *ctx) {
   if (!ctx) return MOE_ERR_INVALID_ARG;
   int dev = -1;
@@ -121,7 +138,9 @@ moe_status check_ctx(moe_ctx *ctx) {
 // format (xa: x itself for f32/bf16, the MX codes for MX-fp8).
 hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *xa,
                const uint8_t *xs, int T, const int32_t *sorted_src, const int32_t *offsets,
-               void *y, void *h, uint8_t *hs, hipStream_t s) {
+               void *y, void *h, uint8_t *hs, hipStream_t s, StageTimer *tm = nullptr) {
+  const int st1 = shared ? MOE_STAGE_SHARED_GATE_UP : MOE_STAGE_GATE_UP;
+  const int st2 = shared ? MOE_STAGE_SHARED_DOWN : MOE_STAGE_DOWN;
   const int F = fmt_of(d->expert_dtype);
   const int H = d->hidden, I = shared ? d->shared_inter : d->inter;
   const int E = shared ? 1 : d->num_experts;
@@ -148,8 +167,11 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g1.out = h;
   g1.out_scale = hs;
   g1.n_out = I;
-  hipError_t err = launch_grouped_gemm(g1, F, EPI_SWIGLU, F, rows, s);
+  hipError_t err;
+  if (tm && (err = tm->start(st1, s)) != hipSuccess) return err;
+  err = launch_grouped_gemm(g1, F, EPI_SWIGLU, F, rows, s);
   if (err != hipSuccess) return err;
+  if (tm && (err = tm->stop(st1, s)) != hipSuccess) return err;
 
   GemmArgs g2;
   memset(&g2, 0, sizeof g2);
@@ -170,7 +192,11 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g2.out = y;
   g2.out_scale = nullptr;
   g2.n_out = H;
-  return launch_grouped_gemm(g2, F, EPI_PLAIN, fmt_of(d->out_dtype), rows, s);
+  if (tm && (err = tm->start(st2, s)) != hipSuccess) return err;
+  err = launch_grouped_gemm(g2, F, EPI_PLAIN, fmt_of(d->out_dtype), rows, s);
+  if (err != hipSuccess) return err;
+  if (tm) err = tm->stop(st2, s);
+  return err;
 }
 
 bool weights_ok(const moe_desc *d, const moe_weights *w, int need_router, int need_routed,
@@ -234,11 +260,49 @@ moe_status moe_ctx_destroy(moe_ctx *ctx) {
   if (!ctx) return MOE_ERR_INVALID_ARG;
   (void)hipEventDestroy(ctx->ev_ready);
   (void)hipEventDestroy(ctx->ev_done);
+  if (ctx->profiling)
+    for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) (void)hipEventDestroy(ctx->prof[i]);
   delete ctx;
   return MOE_OK;
 }
 
 const char *moe_ctx_last_error(const moe_ctx *ctx) { return ctx ? ctx->last_error : ""; }
+
+moe_status moe_ctx_set_profiling(moe_ctx *ctx, int enable) {
+  moe_status st = check_ctx(ctx);
+  if (st != MOE_OK) return st;
+  if (enable && !ctx->profiling) {
+    for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) {
+      hipError_t err = hipEventCreate(&ctx->prof[i]);
+      if (err != hipSuccess) {
+        for (int j = 0; j < i; ++j) (void)hipEventDestroy(ctx->prof[j]);
+        return device_error(ctx, err, "moe_ctx_set_profiling");
+      }
+    }
+    ctx->profiling = 1;
+    ctx->ran = 0;
+  } else if (!enable && ctx->profiling) {
+    for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) (void)hipEventSynchronize(ctx->prof[i]);
+    for (int i = 0; i < 2 * MOE_NUM_STAGES; ++i) (void)hipEventDestroy(ctx->prof[i]);
+    ctx->profiling = 0;
+    ctx->ran = 0;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_ctx_stage_ms(moe_ctx *ctx, float *ms) {
+  moe_status st = check_ctx(ctx);
+  if (st != MOE_OK) return st;
+  if (!ms || !ctx->profiling) return MOE_ERR_INVALID_ARG;
+  for (int i = 0; i < MOE_NUM_STAGES; ++i) {
+    ms[i] = 0.0f;
+    if (!(ctx->ran & (1u << i))) continue;
+    hipError_t err = hipEventSynchronize(ctx->prof[2 * i + 1]);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms[i], ctx->prof[2 * i], ctx->prof[2 * i + 1]);
+    if (err != hipSuccess) return device_error(ctx, err, "moe_ctx_stage_ms");
+  }
+  return MOE_OK;
+}
 
 size_t moe_workspace_bytes(const moe_desc *desc, int32_t T, int which) {
   if (check_desc(desc) != MOE_OK || T < 0 || which < MOE_WS_ROUTE || which > MOE_WS_LAYER) return 0;
@@ -411,6 +475,8 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   int32_t *src = (int32_t *)(b + L.src);
   int32_t *dest = (int32_t *)(b + L.dest);
   hipError_t err;
+  StageTimer tm{ctx};
+  ctx->ran = 0;
 #define MOE_TRY(call, where)                          \
   do {                                                \
     err = (call);                                     \
@@ -418,15 +484,19 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   } while (0)
 
   // Gating on the main stream.
+  MOE_TRY(tm.start(MOE_STAGE_ROUTE, s), "timing");
   MOE_TRY(launch_route(x, desc->act_dtype == MOE_BF16, w->router_w, w->router_bias,
                        (float *)(b + L.logits), idx, tw, T, H, E, k, desc->router_scaling_factor,
                        desc->route_norm, s),
           "gating");
+  MOE_TRY(tm.stop(MOE_STAGE_ROUTE, s), "timing");
   const void *xa = x;
   const uint8_t *xs = nullptr;
   if (mx) {
+    MOE_TRY(tm.start(MOE_STAGE_MX_QUANT, s), "timing");
     MOE_TRY(launch_mx_quantize(x, 1, T, H, (uint8_t *)b + L.xq, (uint8_t *)b + L.xs, s),
             "activation quantisation");
+    MOE_TRY(tm.stop(MOE_STAGE_MX_QUANT, s), "timing");
     xa = b + L.xq;
     xs = (const uint8_t *)b + L.xs;
   }
@@ -439,22 +509,26 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
       MOE_TRY(hipStreamWaitEvent(ss, ctx->ev_ready, 0), "side stream wait");
     }
     MOE_TRY(ffn(desc, w, 1, xa, xs, T, nullptr, nullptr, b + L.z, b + L.sh_h,
-                mx ? (uint8_t *)b + L.sh_hs : nullptr, ss),
+                mx ? (uint8_t *)b + L.sh_hs : nullptr, ss, &tm),
             "shared expert");
     if (two) MOE_TRY(hipEventRecord(ctx->ev_done, ss), "shared-done event");
   }
   // Routed path on the main stream: InitRouting, grouped GEMM.
+  MOE_TRY(tm.start(MOE_STAGE_PERMUTE, s), "timing");
   MOE_TRY(launch_permute(idx, T, E, k, (int32_t *)(b + L.counts), offsets, src, dest, b + L.perm,
                          s),
           "permutation");
+  MOE_TRY(tm.stop(MOE_STAGE_PERMUTE, s), "timing");
   MOE_TRY(ffn(desc, w, 0, xa, xs, T, src, offsets, b + L.y, b + L.h,
-              mx ? (uint8_t *)b + L.hs : nullptr, s),
+              mx ? (uint8_t *)b + L.hs : nullptr, s, &tm),
           "routed experts");
   // Join, then FinalizeRouting + shared add.
   if (two) MOE_TRY(hipStreamWaitEvent(s, ctx->ev_done, 0), "main stream wait");
   const int of = fmt_of(desc->out_dtype);
+  MOE_TRY(tm.start(MOE_STAGE_COMBINE, s), "timing");
   MOE_TRY(launch_combine(b + L.y, of, dest, tw, has_shared ? b + L.z : nullptr, T, H, k, out, of, s),
           "combine");
+  MOE_TRY(tm.stop(MOE_STAGE_COMBINE, s), "timing");
 #undef MOE_TRY
   return MOE_OK;
 }

@@ -108,27 +108,42 @@ __device__ __forceinline__ long long token_of(const GemmArgs &g, int r) {
 }
 
 // ----------------------------------------------------------------------------- skinny
-// Grid: E * (N/16 / (4*NW)) workgroups of 4 waves.  Workgroup (e, group)
-// covers 4*NW consecutive weight blocks; wave w takes NW of them.
+// Grid: segments x groups.  KSW == 1: workgroup (e, group) covers 4*NW
+// consecutive weight blocks, wave w takes NW of them over the whole K axis.
+// KSW == 4: the four waves share the same NW blocks and take every fourth K
+// chunk each; their partial sums meet in LDS and are added in wave order
+// (fixed, so results are deterministic).  With PF = 1 each wave keeps two
+// register sets and loads chunk c + 1 while the matrix cores work on chunk
+// c; with PF = 0 latency is hidden by occupancy instead (fewer registers per
+// wave, more waves per SIMD), which suits the many-expert launches.
 
-template <int F, int EPI, int OT, int NW, int MB>
+template <int F, int NW, int MB>
+struct SkinnyBuf {
+  i32x4 w[NW][4], t[MB][4];
+  uint32_t ws[NW], ts[MB];
+};
+
+template <int F, int EPI, int OT, int NW, int MB, int KSW, int PF>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nbtot = g.N >> 4;
-  const int ngroups = nbtot / (4 * NW);
+  constexpr int BPW = (KSW == 4) ? NW : 4 * NW;       // weight blocks per workgroup
+  const int ngroups = nbtot / BPW;
   const int e = blockIdx.x / ngroups, grp = blockIdx.x % ngroups;
   int s0, s1;
   if (g.offsets) { s0 = g.offsets[e]; s1 = g.offsets[e + 1]; }
   else { s0 = 0; s1 = g.rows; }
   if (s1 <= s0) return;
-  const int nb0 = (grp * 4 + wave) * NW;
+  const int nb0 = (KSW == 4) ? grp * NW : (grp * 4 + wave) * NW;
   const int kcn = g.K / FmtInfo<F>::chunk_elems;     // chunks along K
+  const int k0 = (KSW == 4) ? wave : 0;
   const int grp_l = lane >> 4;
   const uint8_t *wb = g.w + (size_t)e * g.w_expert_stride + (size_t)nb0 * kcn * kBlockBytes +
                       lane * 16;
   const uint16_t *wsb = nullptr;
   if constexpr (F == FMT_MX8)
     wsb = g.w_scale + (size_t)e * g.ws_expert_stride + (size_t)nb0 * kcn * 64 + lane;
+  __shared__ f32x4 red[KSW == 4 ? 3 : 1][KSW == 4 ? NW * MB : 1][64];
 
   for (int mbase = s0; mbase < s1; mbase += 16 * MB) {
     const uint8_t *tp[MB];
@@ -139,6 +154,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       int rr = r < s1 ? r : s1 - 1;
       long long tok = token_of(g, rr);
       tp[i] = g.a + tok * g.a_row_bytes + 16 * grp_l;
+      tsp[i] = nullptr;
       if constexpr (F == FMT_MX8) tsp[i] = g.a_scale + tok * (g.K / 32) + grp_l;
     }
     f32x4 acc[NW][MB];
@@ -147,64 +163,106 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) acc[n][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-
-    for (int kc = 0; kc < kcn; ++kc) {
-      i32x4 wf[NW][4], tf[MB][4];
-      uint32_t wsc[NW], tsc[MB];
+    auto load = [&](SkinnyBuf<F, NW, MB> &bf, int kc) {
 #pragma unroll
       for (int n = 0; n < NW; ++n)
 #pragma unroll
         for (int p = 0; p < 4; ++p)
-          wf[n][p] = __builtin_nontemporal_load(
+          bf.w[n][p] = __builtin_nontemporal_load(
               (const i32x4 *)(wb + ((size_t)n * kcn + kc) * kBlockBytes + p * 1024));
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) tf[i][p] = *(const i32x4 *)(tp[i] + kc * 256 + chunk_off(0, p));
+        for (int p = 0; p < 4; ++p) bf.t[i][p] = *(const i32x4 *)(tp[i] + kc * 256 + chunk_off(0, p));
       if constexpr (F == FMT_MX8) {
 #pragma unroll
-        for (int n = 0; n < NW; ++n) wsc[n] = wsb[((size_t)n * kcn + kc) * 64];
+        for (int n = 0; n < NW; ++n) bf.ws[n] = wsb[((size_t)n * kcn + kc) * 64];
 #pragma unroll
-        for (int i = 0; i < MB; ++i) tsc[i] = tsp[i][8 * kc] | ((uint32_t)tsp[i][8 * kc + 4] << 8);
+        for (int i = 0; i < MB; ++i) bf.ts[i] = tsp[i][8 * kc] | ((uint32_t)tsp[i][8 * kc + 4] << 8);
       } else {
 #pragma unroll
-        for (int n = 0; n < NW; ++n) wsc[n] = 0;
+        for (int n = 0; n < NW; ++n) bf.ws[n] = 0;
 #pragma unroll
-        for (int i = 0; i < MB; ++i) tsc[i] = 0;
+        for (int i = 0; i < MB; ++i) bf.ts[i] = 0;
       }
+    };
+    auto compute = [&](const SkinnyBuf<F, NW, MB> &bf) {
 #pragma unroll
       for (int n = 0; n < NW; ++n)
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
-          mfma_half<F>(acc[n][i], wf[n][0], wf[n][1], tf[i][0], tf[i][1], wsc[n] & 0xFF,
-                       tsc[i] & 0xFF);
-          mfma_half<F>(acc[n][i], wf[n][2], wf[n][3], tf[i][2], tf[i][3], wsc[n] >> 8,
-                       tsc[i] >> 8);
+          mfma_half<F>(acc[n][i], bf.w[n][0], bf.w[n][1], bf.t[i][0], bf.t[i][1], bf.ws[n] & 0xFF,
+                       bf.ts[i] & 0xFF);
+          mfma_half<F>(acc[n][i], bf.w[n][2], bf.w[n][3], bf.t[i][2], bf.t[i][3], bf.ws[n] >> 8,
+                       bf.ts[i] >> 8);
         }
+    };
+
+    if constexpr (PF) {
+      SkinnyBuf<F, NW, MB> b0, b1;
+      if (k0 < kcn) load(b0, k0);
+      for (int kc = k0; kc < kcn; kc += 2 * KSW) {
+        if (kc + KSW < kcn) load(b1, kc + KSW);
+        compute(b0);
+        if (kc + KSW >= kcn) break;
+        if (kc + 2 * KSW < kcn) load(b0, kc + 2 * KSW);
+        compute(b1);
+      }
+    } else {
+      for (int kc = k0; kc < kcn; kc += KSW) {
+        SkinnyBuf<F, NW, MB> b0;
+        load(b0, kc);
+        compute(b0);
+      }
     }
+
+    if constexpr (KSW == 4) {
+      if (wave > 0) {
 #pragma unroll
-    for (int i = 0; i < MB; ++i) {
-      f32x4 col[NW];
+        for (int n = 0; n < NW; ++n)
 #pragma unroll
-      for (int n = 0; n < NW; ++n) col[n] = acc[n][i];
-      const int r = mbase + 16 * i + (lane & 15);
-      epilogue<EPI, OT, NW>(col, nb0, r, r < s1, g, lane);
+          for (int i = 0; i < MB; ++i) red[wave - 1][n * MB + i][lane] = acc[n][i];
+      }
+      __syncthreads();
+      if (wave == 0) {
+#pragma unroll
+        for (int w = 0; w < 3; ++w)
+#pragma unroll
+          for (int n = 0; n < NW; ++n)
+#pragma unroll
+            for (int i = 0; i < MB; ++i) acc[n][i] += red[w][n * MB + i][lane];
+#pragma unroll
+        for (int i = 0; i < MB; ++i) {
+          f32x4 col[NW];
+#pragma unroll
+          for (int n = 0; n < NW; ++n) col[n] = acc[n][i];
+          const int r = mbase + 16 * i + (lane & 15);
+          epilogue<EPI, OT, NW>(col, nb0, r, r < s1, g, lane);
+        }
+      }
+      __syncthreads();
+    } else {
+#pragma unroll
+      for (int i = 0; i < MB; ++i) {
+        f32x4 col[NW];
+#pragma unroll
+        for (int n = 0; n < NW; ++n) col[n] = acc[n][i];
+        const int r = mbase + 16 * i + (lane & 15);
+        epilogue<EPI, OT, NW>(col, nb0, r, r < s1, g, lane);
+      }
     }
   }
 }
 
 // ----------------------------------------------------------------------------- tile map
-// Locate m-tile `mt`: expert e and its rows [row0, row_end).  Uses the
-// segment offsets only (device-resident), 256 threads, scratch >= 1024 ints.
+// m-tiles are numbered expert by expert (TM rows each, the last one of an
+// expert ragged).  tile_scan computes, from the segment offsets alone (they
+// stay on the device), cum[e] = m-tiles of experts 0..e and returns the total;
+// tile_locate maps an m-tile index to its expert and rows.  256 threads,
+// cum holds >= 1024 ints.
 template <int TM>
-__device__ bool find_tile(const GemmArgs &g, int mt, int *cum, int &e, int &row0, int &row_end) {
-  if (!g.offsets) {
-    if (mt >= (g.rows + TM - 1) / TM) return false;
-    e = 0;
-    row0 = mt * TM;
-    row_end = g.rows;
-    return true;
-  }
+__device__ int tile_scan(const GemmArgs &g, int *cum) {
+  if (!g.offsets) return (g.rows + TM - 1) / TM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int wtot[4];
   int v[4], run = 0;
@@ -229,8 +287,18 @@ __device__ bool find_tile(const GemmArgs &g, int mt, int *cum, int &e, int &row0
 #pragma unroll
   for (int i = 0; i < 4; ++i) cum[tid * 4 + i] = before + v[i];
   __syncthreads();
-  const int total = cum[g.E - 1];
-  if (mt >= total) return false;
+  return cum[g.E - 1];
+}
+
+template <int TM>
+__device__ void tile_locate(const GemmArgs &g, const int *cum, int mt, int &e, int &row0,
+                            int &row_end) {
+  if (!g.offsets) {
+    e = 0;
+    row0 = mt * TM;
+    row_end = g.rows;
+    return;
+  }
   int lo = 0, hi = g.E - 1;
   while (lo < hi) {
     int mid = (lo + hi) >> 1;
@@ -241,41 +309,62 @@ __device__ bool find_tile(const GemmArgs &g, int mt, int *cum, int &e, int &row0
   const int first = lo ? cum[lo - 1] : 0;
   row0 = g.offsets[lo] + (mt - first) * TM;
   row_end = g.offsets[lo + 1];
-  return true;
 }
 
 // ----------------------------------------------------------------------------- tile
-// Workgroup tile: TN weight rows (NBT blocks) x TM tokens (MBT blocks); waves
-// arranged WN x WM, each owning NBW x MBW accumulator blocks.  Stages are
-// half-chunks: per stage the weight tile is NBT contiguous 2 KiB pieces and
-// the token tile is one 128-byte line of each of TM rows.
+// LDS slot of (row r16, lane group g) inside token piece p: the 16 slots of
+// a lane group are XOR-permuted so the stores of one wave (8 rows x 4 lane
+// groups x 2 pieces, 16 bytes each) fall into distinct banks, while a wave's
+// fragment read (lane group g reads slots 16 g .. 16 g + 15) stays
+// conflict-free.
+__device__ __forceinline__ int tslot(int r16, int g, int p) {
+  return 16 * g + (r16 ^ ((2 * g + 8 * p) & 15));
+}
 
-template <int F, int EPI, int OT, int TN, int TM, int WN, int WM>
-__global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmArgs g) {
+// Workgroup tile: TN weight rows (NBT blocks) x TM tokens (MBT blocks).  Wave
+// w owns weight blocks [w*NBW, (w+1)*NBW) and all MBT token blocks.  Its
+// weight fragments come straight from global memory into registers (the
+// packed layout makes every wave access one contiguous KiB), one stage
+// ahead; the token tile, which all four waves share, is staged through LDS
+// (double-buffered, one barrier per stage).  A stage is half a K chunk: one
+// 128-byte line of each token row and two 1 KiB pieces of each weight block.
+
+template <int F, int EPI, int OT, int TN, int TM>
+__global__ __launch_bounds__(256, (F == FMT_MX8) ? 1 : 2) void gemm_tile_kernel(GemmArgs g) {
   constexpr int NBT = TN / 16, MBT = TM / 16;
-  constexpr int NBW = NBT / WN, MBW = MBT / WM;
-  constexpr int WBYTES = NBT * 2048, TBYTES = MBT * 2048;
-  constexpr int STAGE = WBYTES + TBYTES;
-  constexpr int WLD = NBT / 2;          // 16-byte weight loads per thread per stage
+  constexpr int NBW = NBT / 4;
+  constexpr int TBYTES = MBT * 2048;    // token bytes per stage
   constexpr int TLD = TM / 32;          // 16-byte token loads per thread per stage
-  static_assert(WN * WM == 4, "4 waves");
-  static_assert(WLD >= 1 && TLD >= 1, "tile too small");
-  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  static_assert(NBT % 4 == 0 && TLD >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TBYTES];
   __shared__ int cum[1024];
-  __shared__ uint8_t wscl[2][NBT * 64];
   __shared__ uint8_t tscl[2][MBT * 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wn = wave % WN, wm = wave / WN;
-  const int logical = xcd_swizzle(blockIdx.x, gridDim.x);
-  const int nt = logical / g.mt_upper, mt = logical % g.mt_upper;
-  if (nt >= g.N / TN) return;
+  // Tile order: m-tile major, n-tile minor, so the n-tiles of one m-tile (which
+  // share its token rows) and the m-tiles of one expert (which share its
+  // weight tiles) run next to each other.  Workgroups are dealt round-robin
+  // to the 8 XCDs; each XCD takes one contiguous range of the actual tiles
+  // (counted on the device), so neighbours meet in the same L2 and the
+  // surplus workgroups of the upper-bound grid are spread over all XCDs.
+  const int ntn = g.N / TN;
+  const int total = tile_scan<TM>(g, cum) * ntn;
+  const int per_xcd = (total + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + local;
+  if (local >= per_xcd || logical >= total) return;
+  const int mt = logical / ntn, nt = logical % ntn;
   int e, row0, row_end;
-  if (!find_tile<TM>(g, mt, cum, e, row0, row_end)) return;
+  tile_locate<TM>(g, cum, mt, e, row0, row_end);
 
   const int kcn = g.K / FmtInfo<F>::chunk_elems;
   const int nstage = 2 * kcn;
-  const uint8_t *wsrc = g.w + (size_t)e * g.w_expert_stride + (size_t)(nt * NBT) * kcn * kBlockBytes;
+  const int nb0 = nt * NBT + wave * NBW;       // this wave's first weight block
+  const uint8_t *wsrc = g.w + (size_t)e * g.w_expert_stride + (size_t)nb0 * kcn * kBlockBytes +
+                        lane * 16;
+  const uint16_t *wss = nullptr;
+  if constexpr (F == FMT_MX8)
+    wss = g.w_scale + (size_t)e * g.ws_expert_stride + (size_t)nb0 * kcn * 64 + lane;
 
   // this thread's token rows (fixed across stages)
   const uint8_t *tsrc[TLD];
@@ -287,19 +376,15 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmArgs g) {
     int r = row0 + rl;
     if (r >= row_end) r = row_end - 1;
     tsrc[i] = g.a + token_of(g, r) * g.a_row_bytes + seg * 16;
-    tdst[i] = WBYTES + (rl >> 4) * 2048 + (seg >> 2) * 1024 + ((rl & 15) + 16 * (seg & 3)) * 16;
+    tdst[i] = (rl >> 4) * 2048 + (seg >> 2) * 1024 + tslot(rl & 15, seg & 3, seg >> 2) * 16;
   }
-  // MX scales: per stage NBT*64 weight-lane bytes and MBT*64 token-lane bytes,
-  // spread over the 256 threads (entry idx = tid + 256 i: block idx / 64,
-  // lane idx % 64).
-  constexpr int WSL = (F == FMT_MX8) ? NBT * 64 / 256 : 1;
-  constexpr int TSL = (F == FMT_MX8) ? MBT * 64 / 256 : 1;
-  static_assert(F != FMT_MX8 || (NBT % 4 == 0 && MBT % 4 == 0), "scale staging");
+  // MX token scales: entry idx = tid + 256 i is (token block idx / 64, lane idx % 64)
+  constexpr int TSL = (F == FMT_MX8) ? (MBT * 64 + 255) / 256 : 1;
   const uint8_t *tss[TSL];
   if constexpr (F == FMT_MX8) {
 #pragma unroll
     for (int i = 0; i < TSL; ++i) {
-      const int idx = tid + 256 * i;
+      const int idx = min(tid + 256 * i, MBT * 64 - 1);
       const int rl = (idx >> 6) * 16 + (idx & 15);
       int r = row0 + rl;
       if (r >= row_end) r = row_end - 1;
@@ -307,133 +392,129 @@ __global__ __launch_bounds__(256, 1) void gemm_tile_kernel(GemmArgs g) {
     }
   }
 
-  i32x4 wreg[WLD], treg[TLD];
-  uint32_t wsreg[WSL], tsreg[TSL];
-  auto load_stage = [&](int s) {
+  i32x4 treg[TLD];
+  uint32_t tsreg[TSL];
+  auto load_tokens = [&](int s) {
     const int kc = s >> 1, h = s & 1;
-#pragma unroll
-    for (int i = 0; i < WLD; ++i) {
-      const int idx = tid + 256 * i;
-      const int blk = idx >> 7, within = idx & 127;
-      wreg[i] = *(const i32x4 *)(wsrc + ((size_t)blk * kcn + kc) * kBlockBytes + h * 2048 +
-                                 within * 16);
-    }
 #pragma unroll
     for (int i = 0; i < TLD; ++i) treg[i] = *(const i32x4 *)(tsrc[i] + kc * 256 + h * 128);
     if constexpr (F == FMT_MX8) {
 #pragma unroll
-      for (int i = 0; i < WSL; ++i) {
-        const int idx = tid + 256 * i;
-        const uint32_t v = g.w_scale[(size_t)e * g.ws_expert_stride +
-                                     ((size_t)(nt * NBT + (idx >> 6)) * kcn + kc) * 64 + (idx & 63)];
-        wsreg[i] = (v >> (8 * h)) & 0xFFu;
-      }
-#pragma unroll
       for (int i = 0; i < TSL; ++i) tsreg[i] = tss[i][8 * kc + 4 * h];
     }
   };
-  auto store_stage = [&](int s) {
-    uint8_t *base = lds + (s & 1) * STAGE;
-#pragma unroll
-    for (int i = 0; i < WLD; ++i) *(i32x4 *)(base + (tid + 256 * i) * 16) = wreg[i];
+  auto store_tokens = [&](int s) {
+    uint8_t *base = lds + (s & 1) * TBYTES;
 #pragma unroll
     for (int i = 0; i < TLD; ++i) *(i32x4 *)(base + tdst[i]) = treg[i];
     if constexpr (F == FMT_MX8) {
 #pragma unroll
-      for (int i = 0; i < WSL; ++i) wscl[s & 1][tid + 256 * i] = (uint8_t)wsreg[i];
+      for (int i = 0; i < TSL; ++i)
+        if (tid + 256 * i < MBT * 64) tscl[s & 1][tid + 256 * i] = (uint8_t)tsreg[i];
+    }
+  };
+  i32x4 wcur[NBW][2], wnext[NBW][2];
+  uint32_t wscur[NBW], wsnext[NBW];
+  auto load_weights = [&](int s, i32x4 (&wr)[NBW][2], uint32_t (&wsr)[NBW]) {
+    const int kc = s >> 1, h = s & 1;
 #pragma unroll
-      for (int i = 0; i < TSL; ++i) tscl[s & 1][tid + 256 * i] = (uint8_t)tsreg[i];
+    for (int n = 0; n < NBW; ++n) {
+      const uint8_t *p = wsrc + ((size_t)n * kcn + kc) * kBlockBytes + h * 2048;
+      wr[n][0] = *(const i32x4 *)p;
+      wr[n][1] = *(const i32x4 *)(p + 1024);
+      wsr[n] = 0;
+      if constexpr (F == FMT_MX8) wsr[n] = (wss[((size_t)n * kcn + kc) * 64] >> (8 * h)) & 0xFFu;
     }
   };
 
-  f32x4 acc[NBW][MBW];
+  f32x4 acc[NBW][MBT];
 #pragma unroll
   for (int n = 0; n < NBW; ++n)
 #pragma unroll
-    for (int m = 0; m < MBW; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MBT; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_stage(0);
-  store_stage(0);
-  if (nstage > 1) load_stage(1);
+  load_tokens(0);
+  load_weights(0, wcur, wscur);
+  store_tokens(0);
+  if (nstage > 1) load_tokens(1);
   __syncthreads();
 
   for (int s = 0; s < nstage; ++s) {
-    const uint8_t *base = lds + (s & 1) * STAGE;
-    i32x4 wf[NBW][2], tf[MBW][2];
-    uint32_t wsc[NBW], tsc[MBW];
+    if (s + 1 < nstage) load_weights(s + 1, wnext, wsnext);
+    const uint8_t *base = lds + (s & 1) * TBYTES;
+#pragma unroll
+    for (int m = 0; m < MBT; ++m) {
+      const uint8_t *p = base + m * 2048;
+      const i32x4 t0 = *(const i32x4 *)(p + tslot(lane & 15, lane >> 4, 0) * 16);
+      const i32x4 t1 = *(const i32x4 *)(p + 1024 + tslot(lane & 15, lane >> 4, 1) * 16);
+      uint32_t ts = 0;
+      if constexpr (F == FMT_MX8) ts = tscl[s & 1][m * 64 + lane];
+#pragma unroll
+      for (int n = 0; n < NBW; ++n)
+        mfma_half<F>(acc[n][m], wcur[n][0], wcur[n][1], t0, t1, wscur[n], ts);
+    }
+    if (s + 1 < nstage) store_tokens(s + 1);
+    if (s + 2 < nstage) load_tokens(s + 2);
+    __syncthreads();
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
-      const uint8_t *p = base + (wn * NBW + n) * 2048 + lane * 16;
-      wf[n][0] = *(const i32x4 *)p;
-      wf[n][1] = *(const i32x4 *)(p + 1024);
-      wsc[n] = 0;
-      if constexpr (F == FMT_MX8) wsc[n] = wscl[s & 1][(wn * NBW + n) * 64 + lane];
+      wcur[n][0] = wnext[n][0];
+      wcur[n][1] = wnext[n][1];
+      wscur[n] = wsnext[n];
     }
-#pragma unroll
-    for (int m = 0; m < MBW; ++m) {
-      const uint8_t *p = base + WBYTES + (wm * MBW + m) * 2048 + lane * 16;
-      tf[m][0] = *(const i32x4 *)p;
-      tf[m][1] = *(const i32x4 *)(p + 1024);
-      tsc[m] = 0;
-      if constexpr (F == FMT_MX8) tsc[m] = tscl[s & 1][(wm * MBW + m) * 64 + lane];
-    }
-#pragma unroll
-    for (int n = 0; n < NBW; ++n)
-#pragma unroll
-      for (int m = 0; m < MBW; ++m)
-        mfma_half<F>(acc[n][m], wf[n][0], wf[n][1], tf[m][0], tf[m][1], wsc[n], tsc[m]);
-    if (s + 1 < nstage) store_stage(s + 1);
-    if (s + 2 < nstage) load_stage(s + 2);
-    __syncthreads();
   }
 
-  const int nb0 = nt * NBT + wn * NBW;
 #pragma unroll
-  for (int m = 0; m < MBW; ++m) {
+  for (int m = 0; m < MBT; ++m) {
     f32x4 col[NBW];
 #pragma unroll
     for (int n = 0; n < NBW; ++n) col[n] = acc[n][m];
-    const int r = row0 + (wm * MBW + m) * 16 + (lane & 15);
+    const int r = row0 + m * 16 + (lane & 15);
     epilogue<EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane);
   }
 }
 
 // ----------------------------------------------------------------------------- dispatch
 
+template <int F, int EPI, int OT, int NW, int MB, int KSW, int PF = 0>
+static hipError_t launch_skinny(const GemmArgs &g, int segs, hipStream_t stream) {
+  constexpr int BPW = (KSW == 4) ? NW : 4 * NW;
+  const int nbtot = g.N / 16;
+  if (nbtot % BPW) return hipErrorInvalidValue;
+  gemm_skinny_kernel<F, EPI, OT, NW, MB, KSW, PF><<<segs * (nbtot / BPW), 256, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
 template <int F, int EPI, int OT>
 static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t stream) {
   GemmArgs g = g0;
   const int segs = g.offsets ? g.E : 1;
-  const int nbtot = g.N / 16;
   // rows per segment: the mean for expert segments, all rows for one segment
   const int per = g.offsets ? (total_rows + segs - 1) / segs : total_rows;
-  if (per <= 64 && nbtot % 16 == 0) {
-    // weight-streaming kernel, 4 weight blocks per wave, MB token blocks
-    const int grid = segs * (nbtot / 16);
-    if (per <= 16)
-      gemm_skinny_kernel<F, EPI, OT, 4, 1><<<grid, 256, 0, stream>>>(g);
-    else if (per <= 32)
-      gemm_skinny_kernel<F, EPI, OT, 4, 2><<<grid, 256, 0, stream>>>(g);
-    else
-      gemm_skinny_kernel<F, EPI, OT, 4, 4><<<grid, 256, 0, stream>>>(g);
-    return hipGetLastError();
+  // weight blocks a SwiGLU workgroup must hold: gate/up pairs (2), and for the
+  // MX-quantising epilogue whole 32-column blocks (4)
+  constexpr int NWS = (EPI == EPI_SWIGLU) ? (OT == FMT_MX8 ? 4 : 2) : 1;
+  if (per <= 64) {
+    if (g.offsets) {
+      // many segments: enough workgroups without splitting K
+      if (per <= 16) return launch_skinny<F, EPI, OT, 4, 1, 1>(g, segs, stream);
+      if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
+      return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
+    }
+    // one segment (shared expert): few weight blocks per workgroup, K split
+    // over the four waves, so the weights spread over many workgroups
+    if (per <= 16) return launch_skinny<F, EPI, OT, NWS, 1, 4>(g, 1, stream);
+    if (per <= 32) return launch_skinny<F, EPI, OT, NWS, 2, 4>(g, 1, stream);
+    return launch_skinny<F, EPI, OT, NWS, 4, 4>(g, 1, stream);
   }
   constexpr int TN = 256, TM = 128;
   if (g.N % TN != 0) return hipErrorInvalidValue;
   const int mtiles = g.offsets ? (total_rows + TM - 1) / TM + g.E : (g.rows + TM - 1) / TM;
   g.mt_upper = mtiles;
+  // upper bound on the tiles, rounded up to whole rounds of the 8 XCDs
   long long nblocks = (long long)mtiles * (g.N / TN);
-  nblocks = (nblocks + 7) & ~7LL;
-  const size_t lds = 2 * (size_t)(TN / 16 + TM / 16) * 2048;
-  auto kern = gemm_tile_kernel<F, EPI, OT, TN, TM, 2, 2>;
-  static bool attr_set = false;
-  if (!attr_set) {
-    hipError_t err = hipFuncSetAttribute((const void *)kern,
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (err != hipSuccess) return err;
-    attr_set = true;
-  }
-  kern<<<(unsigned)nblocks, 256, lds, stream>>>(g);
+  nblocks = ((nblocks + 7) / 8) * 8 + 8;
+  gemm_tile_kernel<F, EPI, OT, TN, TM><<<(unsigned)nblocks, 256, 0, stream>>>(g);
   return hipGetLastError();
 }
 

@@ -135,12 +135,4 @@ __device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32
   }
 }
 
-__device__ __forceinline__ int xcd_swizzle(int bid, int nblocks) {
-  // Workgroups are dispatched round-robin over the 8 XCDs.  Give each XCD a
-  // contiguous range of logical tiles so neighbouring tiles (which share
-  // weights) meet in the same L2.  nblocks must be a multiple of 8.
-  int per = nblocks >> 3;
-  return (bid & 7) * per + (bid >> 3);
-}
-
 }  // namespace moe

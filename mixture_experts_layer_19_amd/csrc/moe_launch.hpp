@@ -38,8 +38,10 @@ enum Epi { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 hipError_t launch_grouped_gemm(const GemmArgs &g, int fmt, int epi, int out_fmt, int total_rows,
                                hipStream_t stream);
 
+// Gating.  part: route_ws_bytes() of scratch for the fp32 partial logits.
+size_t route_ws_bytes(int T, int H, int E, int x_is_bf16);
 hipError_t launch_route(const void *x, int x_is_bf16, const float *Wr, const float *bias,
-                        float *logits, int32_t *topk_idx, float *topk_w, int T, int H, int E, int k,
+                        float *part, int32_t *topk_idx, float *topk_w, int T, int H, int E, int k,
                         float rho, int route_norm, hipStream_t stream);
 
 size_t permute_ws_bytes(int T, int E);

@@ -57,6 +57,8 @@ def _load():
         lib = ctypes.CDLL(_LIB)
         P = ctypes.c_void_p
         I64 = ctypes.c_int64
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
         lib.oracle_e4m3_decode.restype = ctypes.c_double
         lib.oracle_e4m3_decode.argtypes = [ctypes.c_uint8]
         lib.oracle_e4m3_encode.restype = ctypes.c_uint8
@@ -104,6 +106,11 @@ def _weights(w):
 def _check(rc, what):
     if rc != 0:
         raise ValueError("oracle %s rejected its arguments" % what)
+
+
+def num_threads() -> int:
+    """OpenMP threads the oracle's parallel loops use."""
+    return int(_load().oracle_num_threads())
 
 
 # ----------------------------------------------------------------------------- MX-fp8

@@ -29,11 +29,15 @@
  * Error behaviour: functions return 0 on success and -1 on a bad argument.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 #define ORC_EXPORT __attribute__((visibility("default")))
+
+/* Threads an OpenMP region of this library runs with (for reporting). */
+ORC_EXPORT int oracle_num_threads(void) { return omp_get_max_threads(); }
 
 /* ------------------------------------------------------------------ */
 /* Element decoding                                                    */
