@@ -26,14 +26,17 @@ def _hipcc() -> str:
     return p
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+    """Compile csrc/*.hip and link them into `out` (default: the package's
+    libmoe.so).  `defines` are extra -D macros (tuning variants)."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    objdir = os.path.join(HERE, "_build")
+    tag = "_".join(d.replace("=", "") for d in defines)
+    objdir = os.path.join(HERE, "_build" + ("_" + tag if tag else ""))
     os.makedirs(objdir, exist_ok=True)
     flags = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
-             "-Wno-unused-variable"]
+             "-Wno-unused-variable"] + ["-D" + d for d in defines]
     hipcc = _hipcc()
 
     def one(src):
@@ -48,16 +51,21 @@ def build(verbose: bool = False) -> str:
 
     with ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
         objs = list(ex.map(one, srcs))
-    tmp = LIB + ".tmp%d" % os.getpid()
+    tmp = out + ".tmp%d" % os.getpid()
     cmd = [hipcc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + objs
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed:\n%s" % r.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
+    import argparse
     import time
+    ap = argparse.ArgumentParser()
+    ap.add_argument("-D", dest="defines", action="append", default=[])
+    ap.add_argument("-o", dest="out", default=LIB)
+    a = ap.parse_args()
     t = time.time()
-    print(build(verbose=True), "%.1fs" % (time.time() - t))
+    print(build(verbose=True, defines=a.defines, out=a.out), "%.1fs" % (time.time() - t))

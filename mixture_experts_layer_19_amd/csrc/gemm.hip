@@ -22,6 +22,10 @@
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
 
+#ifndef MOE_TILE_MAP
+#define MOE_TILE_MAP 0
+#endif
+
 namespace moe {
 
 __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
@@ -349,10 +353,15 @@ __global__ __launch_bounds__(256, (F == FMT_MX8) ? 1 : 2) void gemm_tile_kernel(
   // surplus workgroups of the upper-bound grid are spread over all XCDs.
   const int ntn = g.N / TN;
   const int total = tile_scan<TM>(g, cum) * ntn;
+#if MOE_TILE_MAP == 0
   const int per_xcd = (total + 7) >> 3;
   const int local = blockIdx.x >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + local;
   if (local >= per_xcd || logical >= total) return;
+#else
+  const int logical = blockIdx.x;
+  if (logical >= total) return;
+#endif
   const int mt = logical / ntn, nt = logical % ntn;
   int e, row0, row_end;
   tile_locate<TM>(g, cum, mt, e, row0, row_end);
