@@ -52,6 +52,31 @@ def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per launch of the decode gate/up kernel from the committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel's
+    source has changed since those counters were taken."""
+    import hashlib
+    if workload != "hy3_decode":
+        return None
+    path = os.path.join(ROOT, "profiles", "hy3_decode_gate_up_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if line.startswith("#") or ":" not in line:
+            continue
+        k, v = line.split(":", 1)
+        kv[k.strip()] = v.strip()
+    h = hashlib.sha256()
+    for f in ("mixture_experts_layer_19_amd/csrc/gemm.hip",
+              "mixture_experts_layer_19_amd/csrc/moe_common.hpp"):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if kv.get("source_sha256") != h.hexdigest():
+        return None
+    return int(kv["traffic_bytes"])
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -147,7 +172,8 @@ def main():
         roof = {"bound": "hbm", "kernel": "routed gate/up + SwiGLU grouped GEMM",
                 "achieved": round(gu_bytes / (gu_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
                 "unit": "GB/s", "frac": round(gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                "traffic": None, "kernel_ms": round(gu_ms, 4), "algorithmic_bytes": int(gu_bytes)}
+                "traffic": measured_traffic(w.name), "kernel_ms": round(gu_ms, 4),
+                "algorithmic_bytes": int(gu_bytes)}
     result = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
