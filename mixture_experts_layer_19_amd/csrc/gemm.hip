@@ -25,6 +25,10 @@
 #ifndef MOE_TILE_MAP
 #define MOE_TILE_MAP 0
 #endif
+// tiled kernel with the direct-to-LDS operand ring (bf16 / fp32)
+#ifndef MOE_TILE_DMA
+#define MOE_TILE_DMA 0
+#endif
 
 namespace moe {
 
@@ -137,7 +141,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   int s0, s1;
   if (g.offsets) { s0 = g.offsets[e]; s1 = g.offsets[e + 1]; }
   else { s0 = 0; s1 = g.rows; }
-  if (s1 <= s0) return;
+  if (s1 <= s0 || (g.split > 0 && s1 - s0 > g.split)) return;
   const int nb0 = (KSW == 4) ? grp * NW : (grp * 4 + wave) * NW;
   const int kcn = g.K / FmtInfo<F>::chunk_elems;     // chunks along K
   const int k0 = (KSW == 4) ? wave : 0;
@@ -150,6 +154,9 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   __shared__ f32x4 red[KSW == 4 ? 3 : 1][KSW == 4 ? NW * MB : 1][64];
 
   for (int mbase = s0; mbase < s1; mbase += 16 * MB) {
+    // token blocks of this pass that hold rows (uniform): the others are
+    // neither loaded nor multiplied
+    const int live = min(MB, (s1 - mbase + 15) / 16);
     const uint8_t *tp[MB];
     const uint8_t *tsp[MB];
 #pragma unroll
@@ -176,13 +183,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
               (const i32x4 *)(wb + ((size_t)n * kcn + kc) * kBlockBytes + p * 1024));
 #pragma unroll
       for (int i = 0; i < MB; ++i)
+        if (i < live)
 #pragma unroll
-        for (int p = 0; p < 4; ++p) bf.t[i][p] = *(const i32x4 *)(tp[i] + kc * 256 + chunk_off(0, p));
+          for (int p = 0; p < 4; ++p) bf.t[i][p] = *(const i32x4 *)(tp[i] + kc * 256 + chunk_off(0, p));
       if constexpr (F == FMT_MX8) {
 #pragma unroll
         for (int n = 0; n < NW; ++n) bf.ws[n] = wsb[((size_t)n * kcn + kc) * 64];
 #pragma unroll
-        for (int i = 0; i < MB; ++i) bf.ts[i] = tsp[i][8 * kc] | ((uint32_t)tsp[i][8 * kc + 4] << 8);
+        for (int i = 0; i < MB; ++i)
+          if (i < live) bf.ts[i] = tsp[i][8 * kc] | ((uint32_t)tsp[i][8 * kc + 4] << 8);
       } else {
 #pragma unroll
         for (int n = 0; n < NW; ++n) bf.ws[n] = 0;
@@ -195,6 +204,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       for (int n = 0; n < NW; ++n)
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
+          if (i >= live) continue;
           mfma_half<F>(acc[n][i], bf.w[n][0], bf.w[n][1], bf.t[i][0], bf.t[i][1], bf.ws[n] & 0xFF,
                        bf.ts[i] & 0xFF);
           mfma_half<F>(acc[n][i], bf.w[n][2], bf.w[n][3], bf.t[i][2], bf.t[i][3], bf.ws[n] >> 8,
@@ -273,7 +283,8 @@ __device__ int tile_scan(const GemmArgs &g, int *cum) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int ex = tid * 4 + i;
-    const int c = ex < g.E ? g.offsets[ex + 1] - g.offsets[ex] : 0;
+    int c = ex < g.E ? g.offsets[ex + 1] - g.offsets[ex] : 0;
+    if (c <= g.split) c = 0;                 // left to the streaming kernel
     run += (c + TM - 1) / TM;
     v[i] = run;
   }
@@ -483,6 +494,148 @@ __global__ __launch_bounds__(256, (F == FMT_MX8) ? 1 : 2) void gemm_tile_kernel(
   }
 }
 
+// ----------------------------------------------------------------------------- tile (LDS ring)
+// Same tile and wave roles as gemm_tile_kernel, but both operands reach LDS
+// through direct global->LDS loads (global_load_lds_dwordx4: each wave
+// instruction fills one contiguous KiB, lane l's 16 bytes at slot l) into a
+// ring of NS stages, so NS - 1 stages of loads are in flight while the
+// matrix cores work and no registers are tied up by them.  Each wave loads
+// its own weight pieces and a quarter of the token pieces.  Stage s is
+// consumed after this wave's loads for it have landed (vmcnt) and all waves
+// have met at a barrier (so the other waves' token pieces are in too); the
+// ring slot of stage s - 1 is refilled only after that barrier, once every
+// wave has finished reading it.  The barrier is the bare s_barrier with a
+// compiler memory clobber on each side: the ordering the pipeline needs is
+// given by the explicit waits, and a full workgroup fence would drain every
+// load in flight.
+
+#define MOE_GPTR(p) ((__attribute__((address_space(1))) void *)(p))
+#define MOE_LPTR(p) ((__attribute__((address_space(3))) void *)(p))
+
+// s_waitcnt with vmcnt(V) and lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and
+// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8)
+template <int V>
+__device__ __forceinline__ void wait_vm_lgkm0() {
+  static_assert(V >= 0 && V < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4));
+}
+
+__device__ __forceinline__ void ring_barrier() {
+  __asm__ volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  __asm__ volatile("" ::: "memory");
+}
+
+template <int F, int EPI, int OT, int TN, int TM, int NS>
+__global__ __launch_bounds__(256, 1) void gemm_tile_dma_kernel(GemmArgs g) {
+  constexpr int NBT = TN / 16, MBT = TM / 16;
+  constexpr int NBW = NBT / 4;                 // weight blocks per wave
+  constexpr int WST = NBT * 2048, TST = MBT * 2048, STAGE = WST + TST;
+  constexpr int TPW = MBT * 2 / 4;             // token pieces loaded per wave per stage
+  constexpr int LPS = NBW * 2 + TPW;           // loads per wave per stage
+  static_assert(F != FMT_MX8, "MX uses gemm_tile_kernel");
+  static_assert(NBT % 4 == 0 && (MBT * 2) % 4 == 0 && NS >= 2, "tile shape");
+  static_assert((NS - 2) * LPS < 64, "vmcnt range");
+  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];   // NS * STAGE
+  __shared__ int cum[1024];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntn = g.N / TN;
+  const int total = tile_scan<TM>(g, cum) * ntn;
+#if MOE_TILE_MAP == 0
+  const int per_xcd = (total + 7) >> 3;
+  const int local = blockIdx.x >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + local;
+  if (local >= per_xcd || logical >= total) return;
+#else
+  const int logical = blockIdx.x;
+  if (logical >= total) return;
+#endif
+  const int mt = logical / ntn, nt = logical % ntn;
+  int e, row0, row_end;
+  tile_locate<TM>(g, cum, mt, e, row0, row_end);
+
+  const int kcn = g.K / FmtInfo<F>::chunk_elems;
+  const int nstage = 2 * kcn;
+  const int nb0 = nt * NBT + wave * NBW;
+  const uint8_t *wsrc = g.w + (size_t)e * g.w_expert_stride + (size_t)nb0 * kcn * kBlockBytes +
+                        lane * 16;
+  // token pieces this wave loads: q = wave * TPW + i -> block q / 2, piece q % 2
+  const uint8_t *tsrc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int q = wave * TPW + i;
+    const int rl = (q >> 1) * 16 + (lane & 15);
+    int r = row0 + rl;
+    if (r >= row_end) r = row_end - 1;
+    tsrc[i] = g.a + token_of(g, r) * g.a_row_bytes + 64 * (q & 1) + 16 * (lane >> 4);
+  }
+
+  auto issue = [&](int s) {
+    const int kc = s >> 1, h = s & 1;
+    uint8_t *st = ring + (s % NS) * STAGE;
+#pragma unroll
+    for (int n = 0; n < NBW; ++n)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        __builtin_amdgcn_global_load_lds(
+            MOE_GPTR(wsrc + ((size_t)n * kcn + kc) * kBlockBytes + (2 * h + pp) * 1024),
+            MOE_LPTR(st + (wave * NBW + n) * 2048 + pp * 1024), 16, 0, 0);
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+      const int q = wave * TPW + i;
+      __builtin_amdgcn_global_load_lds(MOE_GPTR(tsrc[i] + kc * 256 + h * 128),
+                                       MOE_LPTR(st + WST + (q >> 1) * 2048 + (q & 1) * 1024),
+                                       16, 0, 0);
+    }
+  };
+
+  f32x4 acc[NBW][MBT];
+#pragma unroll
+  for (int n = 0; n < NBW; ++n)
+#pragma unroll
+    for (int m = 0; m < MBT; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int q = 0; q < NS - 1; ++q)
+    if (q < nstage) issue(q);
+
+  for (int s = 0; s < nstage; ++s) {
+    // this wave's loads for stage s are the oldest still counted: allow the
+    // later stages' loads (at most NS - 2 of them) to stay in flight
+    if (s + NS - 2 < nstage) wait_vm_lgkm0<(NS - 2) * LPS>();
+    else wait_vm_lgkm0<0>();
+    ring_barrier();
+    if (s + NS - 1 < nstage) issue(s + NS - 1);
+    const uint8_t *st = ring + (s % NS) * STAGE;
+    i32x4 wf[NBW][2], tf[MBT][2];
+#pragma unroll
+    for (int n = 0; n < NBW; ++n)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        wf[n][pp] = *(const i32x4 *)(st + (wave * NBW + n) * 2048 + pp * 1024 + lane * 16);
+#pragma unroll
+    for (int m = 0; m < MBT; ++m)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp)
+        tf[m][pp] = *(const i32x4 *)(st + WST + m * 2048 + pp * 1024 + lane * 16);
+#pragma unroll
+    for (int m = 0; m < MBT; ++m)
+#pragma unroll
+      for (int n = 0; n < NBW; ++n)
+        mfma_half<F>(acc[n][m], wf[n][0], wf[n][1], tf[m][0], tf[m][1], 0, 0);
+  }
+
+#pragma unroll
+  for (int m = 0; m < MBT; ++m) {
+    f32x4 col[NBW];
+#pragma unroll
+    for (int n = 0; n < NBW; ++n) col[n] = acc[n][m];
+    const int r = row0 + m * 16 + (lane & 15);
+    epilogue<EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane);
+  }
+}
+
 // ----------------------------------------------------------------------------- dispatch
 
 template <int F, int EPI, int OT, int NW, int MB, int KSW, int PF = 0>
@@ -503,18 +656,24 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
   // weight blocks a SwiGLU workgroup must hold: gate/up pairs (2), and for the
   // MX-quantising epilogue whole 32-column blocks (4)
   constexpr int NWS = (EPI == EPI_SWIGLU) ? (OT == FMT_MX8 ? 4 : 2) : 1;
-  if (per <= 64) {
-    if (g.offsets) {
-      // many segments: enough workgroups without splitting K
-      if (per <= 16) return launch_skinny<F, EPI, OT, 4, 1, 1>(g, segs, stream);
-      if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
-      return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
-    }
+  if (!g.offsets) {
     // one segment (shared expert): few weight blocks per workgroup, K split
     // over the four waves, so the weights spread over many workgroups
     if (per <= 16) return launch_skinny<F, EPI, OT, NWS, 1, 4>(g, 1, stream);
     if (per <= 32) return launch_skinny<F, EPI, OT, NWS, 2, 4>(g, 1, stream);
-    return launch_skinny<F, EPI, OT, NWS, 4, 4>(g, 1, stream);
+    if (per <= 64) return launch_skinny<F, EPI, OT, NWS, 4, 4>(g, 1, stream);
+  } else if (g.rows <= 64 * g.k_route) {
+    // at most T <= 64 rows per expert: the streaming kernel takes them all
+    if (per <= 16) return launch_skinny<F, EPI, OT, 4, 1, 1>(g, segs, stream);
+    if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
+    return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
+  } else {
+    // experts of at most 64 rows go to the streaming kernel, the longer
+    // ones to the tiled kernel (the split is applied on the device, where
+    // the counts are)
+    g.split = 64;
+    hipError_t err = launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
+    if (err != hipSuccess) return err;
   }
   constexpr int TN = 256, TM = 128;
   if (g.N % TN != 0) return hipErrorInvalidValue;
@@ -523,6 +682,22 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
   // upper bound on the tiles, rounded up to whole rounds of the 8 XCDs
   long long nblocks = (long long)mtiles * (g.N / TN);
   nblocks = ((nblocks + 7) / 8) * 8 + 8;
+#if MOE_TILE_DMA
+  if constexpr (F != FMT_MX8) {
+    constexpr int NS = 3;
+    const size_t lds = (size_t)NS * (TN / 16 + TM / 16) * 2048;
+    auto kern = gemm_tile_dma_kernel<F, EPI, OT, TN, TM, NS>;
+    static bool attr_set = false;
+    if (!attr_set) {
+      hipError_t err = hipFuncSetAttribute((const void *)kern,
+                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (err != hipSuccess) return err;
+      attr_set = true;
+    }
+    kern<<<(unsigned)nblocks, 256, lds, stream>>>(g);
+    return hipGetLastError();
+  }
+#endif
   gemm_tile_kernel<F, EPI, OT, TN, TM><<<(unsigned)nblocks, 256, 0, stream>>>(g);
   return hipGetLastError();
 }

@@ -28,6 +28,8 @@ struct GemmArgs {
   uint8_t *out_scale;         // MX output scales [rows][n_out/32]
   int n_out;                  // output columns: N/2 for SwiGLU, N otherwise
   int mt_upper;               // tile kernel: m-tiles in the grid
+  int split;                  // > 0: the streaming kernel takes segments of at most
+                              // `split` rows and the tiled kernel the longer ones
 };
 
 enum Epi { EPI_SWIGLU = 0, EPI_PLAIN = 1 };

@@ -260,12 +260,15 @@ def _ffn_case(orc, ctx, w, T, tag, shared=False, idx=None):
     ("f32", 256, 128, 4, 2, 300),       # tiled kernel, several m-tiles + ragged tail
     ("bf16", 512, 256, 12, 4, 30),      # streaming
     ("bf16", 512, 256, 3, 2, 400),      # tiled
+    ("bf16", 512, 256, 12, 2, 300),     # mixed: short experts streamed, long ones tiled
+    ("f32", 256, 128, 12, 2, 300),      # mixed, fp32
     # MX at the workloads' intermediate size: the scaled fp8 MFMA sums with
     # ~1e-5 relative error, so a few SwiGLU outputs land one E4M3 code away
     # from the oracle's; at I = 1536 that stays far inside 3e-2, at small I
     # one such code on a large h element is a larger share of max|y|
     ("mxfp8", 1024, 1536, 12, 4, 30),   # streaming, MX
     ("mxfp8", 1024, 1536, 3, 2, 400),   # tiled, MX
+    ("mxfp8", 1024, 1536, 12, 2, 300),  # mixed, MX
 ])
 def test_grouped_ffn_parity(orc, ctx, dtype, H, I_, E, k, T):
     w = I.Workload("ffn", T=T, H=H, E=E, k=k, I=I_, Is=I_, dtype=dtype)
