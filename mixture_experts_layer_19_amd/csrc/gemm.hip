@@ -25,6 +25,13 @@
 #ifndef MOE_TILE_MAP
 #define MOE_TILE_MAP 0
 #endif
+// token rows per tile and stages of weight prefetch of the MX-fp8 tiled kernel
+#ifndef MOE_TILE_TM_MX
+#define MOE_TILE_TM_MX 64
+#endif
+#ifndef MOE_TILE_WPF_MX
+#define MOE_TILE_WPF_MX 1
+#endif
 // tiled kernel with the direct-to-LDS operand ring (bf16 / fp32)
 #ifndef MOE_TILE_DMA
 #define MOE_TILE_DMA 0
@@ -344,8 +351,8 @@ __device__ __forceinline__ int tslot(int r16, int g, int p) {
 // (double-buffered, one barrier per stage).  A stage is half a K chunk: one
 // 128-byte line of each token row and two 1 KiB pieces of each weight block.
 
-template <int F, int EPI, int OT, int TN, int TM>
-__global__ __launch_bounds__(256, (F == FMT_MX8) ? 1 : 2) void gemm_tile_kernel(GemmArgs g) {
+template <int F, int EPI, int OT, int TN, int TM, int WPF>
+__global__ __launch_bounds__(256, (WPF > 1 || (F == FMT_MX8 && TM > 64)) ? 1 : 2) void gemm_tile_kernel(GemmArgs g) {
   constexpr int NBT = TN / 16, MBT = TM / 16;
   constexpr int NBW = NBT / 4;
   constexpr int TBYTES = MBT * 2048;    // token bytes per stage
@@ -433,17 +440,25 @@ __global__ __launch_bounds__(256, (F == FMT_MX8) ? 1 : 2) void gemm_tile_kernel(
         if (tid + 256 * i < MBT * 64) tscl[s & 1][tid + 256 * i] = (uint8_t)tsreg[i];
     }
   };
-  i32x4 wcur[NBW][2], wnext[NBW][2];
-  uint32_t wscur[NBW], wsnext[NBW];
-  auto load_weights = [&](int s, i32x4 (&wr)[NBW][2], uint32_t (&wsr)[NBW]) {
+  // weight fragments of WPF + 1 stages live in registers: stage s uses set
+  // s % (WPF + 1) while the loads of the next WPF stages are in flight
+  constexpr int NSET = WPF + 1;
+  i32x4 wr[NSET][NBW][2];
+  uint32_t wsr[NSET][NBW];
+  auto load_weights = [&](int s, int set) {
     const int kc = s >> 1, h = s & 1;
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
       const uint8_t *p = wsrc + ((size_t)n * kcn + kc) * kBlockBytes + h * 2048;
-      wr[n][0] = *(const i32x4 *)p;
-      wr[n][1] = *(const i32x4 *)(p + 1024);
-      wsr[n] = 0;
-      if constexpr (F == FMT_MX8) wsr[n] = (wss[((size_t)n * kcn + kc) * 64] >> (8 * h)) & 0xFFu;
+#pragma unroll
+      for (int q = 0; q < NSET; ++q)
+        if (q == set) {
+          wr[q][n][0] = *(const i32x4 *)p;
+          wr[q][n][1] = *(const i32x4 *)(p + 1024);
+          wsr[q][n] = 0;
+          if constexpr (F == FMT_MX8)
+            wsr[q][n] = (wss[((size_t)n * kcn + kc) * 64] >> (8 * h)) & 0xFFu;
+        }
     }
   };
 
@@ -453,14 +468,8 @@ __global__ __launch_bounds__(256, (F == FMT_MX8) ? 1 : 2) void gemm_tile_kernel(
 #pragma unroll
     for (int m = 0; m < MBT; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  load_tokens(0);
-  load_weights(0, wcur, wscur);
-  store_tokens(0);
-  if (nstage > 1) load_tokens(1);
-  __syncthreads();
-
-  for (int s = 0; s < nstage; ++s) {
-    if (s + 1 < nstage) load_weights(s + 1, wnext, wsnext);
+  auto stage = [&](int s, int set) {
+    if (s + WPF < nstage) load_weights(s + WPF, (set + WPF) % NSET);
     const uint8_t *base = lds + (s & 1) * TBYTES;
 #pragma unroll
     for (int m = 0; m < MBT; ++m) {
@@ -471,17 +480,29 @@ __global__ __launch_bounds__(256, (F == FMT_MX8) ? 1 : 2) void gemm_tile_kernel(
       if constexpr (F == FMT_MX8) ts = tscl[s & 1][m * 64 + lane];
 #pragma unroll
       for (int n = 0; n < NBW; ++n)
-        mfma_half<F>(acc[n][m], wcur[n][0], wcur[n][1], t0, t1, wscur[n], ts);
+#pragma unroll
+        for (int q = 0; q < NSET; ++q)
+          if (q == set) mfma_half<F>(acc[n][m], wr[q][n][0], wr[q][n][1], t0, t1, wsr[q][n], ts);
     }
     if (s + 1 < nstage) store_tokens(s + 1);
     if (s + 2 < nstage) load_tokens(s + 2);
     __syncthreads();
+  };
+
+  load_tokens(0);
 #pragma unroll
-    for (int n = 0; n < NBW; ++n) {
-      wcur[n][0] = wnext[n][0];
-      wcur[n][1] = wnext[n][1];
-      wscur[n] = wsnext[n];
-    }
+  for (int q = 0; q < WPF; ++q)
+    if (q < nstage) load_weights(q, q);
+  store_tokens(0);
+  if (nstage > 1) load_tokens(1);
+  __syncthreads();
+
+  // the stage loop, unrolled by the number of register sets so every set
+  // index is a compile-time constant
+  for (int s0 = 0; s0 < nstage; s0 += NSET) {
+#pragma unroll
+    for (int q = 0; q < NSET; ++q)
+      if (s0 + q < nstage) stage(s0 + q, q);
   }
 
 #pragma unroll
@@ -675,7 +696,7 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     hipError_t err = launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
     if (err != hipSuccess) return err;
   }
-  constexpr int TN = 256, TM = 128;
+  constexpr int TN = 256, TM = (F == FMT_MX8) ? MOE_TILE_TM_MX : 128;
   if (g.N % TN != 0) return hipErrorInvalidValue;
   const int mtiles = g.offsets ? (total_rows + TM - 1) / TM + g.E : (g.rows + TM - 1) / TM;
   g.mt_upper = mtiles;
@@ -698,7 +719,8 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     return hipGetLastError();
   }
 #endif
-  gemm_tile_kernel<F, EPI, OT, TN, TM><<<(unsigned)nblocks, 256, 0, stream>>>(g);
+  constexpr int WPF = (F == FMT_MX8) ? MOE_TILE_WPF_MX : 1;
+  gemm_tile_kernel<F, EPI, OT, TN, TM, WPF><<<(unsigned)nblocks, 256, 0, stream>>>(g);
   return hipGetLastError();
 }
 

@@ -106,9 +106,9 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 
 __device__ __forceinline__ int chunk_off(int g, int p) { return 128 * (p >> 1) + 64 * (p & 1) + 16 * g; }
 
-// acc += W x T over one half-chunk.  w, t: the lane's two 16-byte pieces of
-// this half.  ws, ts: E8M0 scale bytes of the lane's MX block in bits 7:0
-// (MX only; opsel 0 selects them).
+// acc += W x T over one half-chunk.  w0, w1 / t0, t1: the lane's two
+// 16-byte pieces of this half (pieces 2h and 2h + 1).  ws, ts: E8M0 scale
+// bytes of the lane's MX block in bits 7:0 (MX only; opsel 0 selects them).
 template <int F>
 __device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32x4 &w1,
                                           const i32x4 &t0, const i32x4 &t1, uint32_t ws,
@@ -128,8 +128,8 @@ __device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(w1[e]), __int_as_float(t1[e]), acc,
                                                  0, 0, 0);
   } else {
-    i32x8 a = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
-    i32x8 b = {t0[0], t0[1], t0[2], t0[3], t1[0], t1[1], t1[2], t1[3]};
+    const i32x8 a = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const i32x8 b = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
     // operand format 0 = fp8 E4M3 for A and B; opsel 0 = scale byte 0
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, (int)ws, 0, (int)ts);
   }
