@@ -43,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--single-stream", action="store_true",
+                    help="run the shared expert on the main stream (per-stage times then "
+                         "measure each kernel alone)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     return ap.parse_args()
@@ -100,7 +103,7 @@ def main():
     Wr, bias = I.router_weight(w), I.router_bias(w)
     log("uploading and packing (%.1fs)" % (time.time() - t0))
     lay = DeviceLayer(w, expert_fn=lambda e: (Wg[e], Wu[e], Wd[e]), shared_fn=lambda: shared,
-                      router=(Wr, bias))
+                      router=(Wr, bias), side_stream=not a.single_stream)
     main_stream = torch.cuda.current_stream(dev)
 
     def run(x_dev, T, steps, warmup):

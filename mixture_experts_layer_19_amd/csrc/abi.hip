@@ -157,6 +157,7 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g1.a = (const uint8_t *)xa;
   g1.a_scale = xs;
   g1.a_row_bytes = (long long)H * eb;
+  g1.a_bytes = (long long)T * H * (long long)eb;
   g1.sorted_src = shared ? nullptr : sorted_src;
   g1.k_route = d->top_k;
   g1.offsets = shared ? nullptr : offsets;
@@ -182,6 +183,7 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g2.a = (const uint8_t *)h;
   g2.a_scale = hs;
   g2.a_row_bytes = (long long)I * eb;
+  g2.a_bytes = (long long)rows * I * (long long)eb;
   g2.sorted_src = nullptr;
   g2.k_route = d->top_k;
   g2.offsets = shared ? nullptr : offsets;
@@ -483,16 +485,10 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
     if (err != hipSuccess) return device_error(ctx, err, where); \
   } while (0)
 
-  // Gating on the main stream.
-  MOE_TRY(tm.start(MOE_STAGE_ROUTE, s), "timing");
-  MOE_TRY(launch_route(x, desc->act_dtype == MOE_BF16, w->router_w, w->router_bias,
-                       (float *)(b + L.logits), idx, tw, T, H, E, k, desc->router_scaling_factor,
-                       desc->route_norm, s),
-          "gating");
-  MOE_TRY(tm.stop(MOE_STAGE_ROUTE, s), "timing");
   const void *xa = x;
   const uint8_t *xs = nullptr;
   if (mx) {
+    // the expert-format activations feed both the shared and the routed experts
     MOE_TRY(tm.start(MOE_STAGE_MX_QUANT, s), "timing");
     MOE_TRY(launch_mx_quantize(x, 1, T, H, (uint8_t *)b + L.xq, (uint8_t *)b + L.xs, s),
             "activation quantisation");
@@ -500,7 +496,8 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
     xa = b + L.xq;
     xs = (const uint8_t *)b + L.xs;
   }
-  // Shared expert: on the side stream once the main stream is past gating.
+  // Shared expert: it needs only the activations, so the side stream starts
+  // it at once and it runs beside gating, permutation and the routed GEMMs.
   const bool two = has_shared && ctx->side && ctx->side != s;
   if (has_shared) {
     hipStream_t ss = two ? ctx->side : s;
@@ -513,6 +510,13 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
             "shared expert");
     if (two) MOE_TRY(hipEventRecord(ctx->ev_done, ss), "shared-done event");
   }
+  // Gating on the main stream.
+  MOE_TRY(tm.start(MOE_STAGE_ROUTE, s), "timing");
+  MOE_TRY(launch_route(x, desc->act_dtype == MOE_BF16, w->router_w, w->router_bias,
+                       (float *)(b + L.logits), idx, tw, T, H, E, k, desc->router_scaling_factor,
+                       desc->route_norm, s),
+          "gating");
+  MOE_TRY(tm.stop(MOE_STAGE_ROUTE, s), "timing");
   // Routed path on the main stream: InitRouting, grouped GEMM.
   MOE_TRY(tm.start(MOE_STAGE_PERMUTE, s), "timing");
   MOE_TRY(launch_permute(idx, T, E, k, (int32_t *)(b + L.counts), offsets, src, dest, b + L.perm,

@@ -25,16 +25,40 @@
 #ifndef MOE_TILE_MAP
 #define MOE_TILE_MAP 0
 #endif
-// token rows per tile and stages of weight prefetch of the MX-fp8 tiled kernel
+// m-tiles per group in the tiled kernel's tile order
+#ifndef MOE_TILE_GM
+#define MOE_TILE_GM 8
+#endif
+// tiled kernel (f32 / bf16): token rows per tile, stages of weight
+// prefetch, workgroups per CU it is compiled for
+#ifndef MOE_TILE_TM
+#define MOE_TILE_TM 128
+#endif
+#ifndef MOE_TILE_WPF
+#define MOE_TILE_WPF 1
+#endif
+#ifndef MOE_TILE_OCC
+#define MOE_TILE_OCC 2
+#endif
+// waves per workgroup of the tiled kernel (64 weight rows each) and the
+// cache-policy bits of its weight loads
+#ifndef MOE_TILE_NWV
+#define MOE_TILE_NWV 4
+#endif
+#ifndef MOE_TILE_WAUX
+#define MOE_TILE_WAUX 0
+#endif
+// pin the interleaving of LDS reads and products with scheduling groups
+#ifndef MOE_TILE_SGB
+#define MOE_TILE_SGB 0
+#endif
+// workgroups per CU the MX-fp8 tiled kernel is compiled for
+#ifndef MOE_TILE_OCC_MX
+#define MOE_TILE_OCC_MX 2
+#endif
+// token rows per tile of the MX-fp8 tiled kernel
 #ifndef MOE_TILE_TM_MX
 #define MOE_TILE_TM_MX 64
-#endif
-#ifndef MOE_TILE_WPF_MX
-#define MOE_TILE_WPF_MX 1
-#endif
-// tiled kernel with the direct-to-LDS operand ring (bf16 / fp32)
-#ifndef MOE_TILE_DMA
-#define MOE_TILE_DMA 0
 #endif
 
 namespace moe {
@@ -279,58 +303,81 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 // m-tiles are numbered expert by expert (TM rows each, the last one of an
 // expert ragged).  tile_scan computes, from the segment offsets alone (they
 // stay on the device), cum[e] = m-tiles of experts 0..e and returns the total;
-// tile_locate maps an m-tile index to its expert and rows.  256 threads,
-// cum holds >= 1024 ints.
+// tile_locate below maps a tile index to its expert, rows and n-tile.  At
+// least 256 threads; cum holds >= 1024 ints.
 template <int TM>
 __device__ int tile_scan(const GemmArgs &g, int *cum) {
   if (!g.offsets) return (g.rows + TM - 1) / TM;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   __shared__ int wtot[4];
   int v[4], run = 0;
+  if (tid < 256) {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int ex = tid * 4 + i;
-    int c = ex < g.E ? g.offsets[ex + 1] - g.offsets[ex] : 0;
-    if (c <= g.split) c = 0;                 // left to the streaming kernel
-    run += (c + TM - 1) / TM;
-    v[i] = run;
+    for (int i = 0; i < 4; ++i) {
+      const int ex = tid * 4 + i;
+      int c = ex < g.E ? g.offsets[ex + 1] - g.offsets[ex] : 0;
+      if (c <= g.split) c = 0;               // left to the streaming kernel
+      run += (c + TM - 1) / TM;
+      v[i] = run;
+    }
   }
-  // inclusive scan of per-thread totals: within the wave, then across waves
+  // inclusive scan of per-thread totals: within the wave, then across the
+  // first four waves (threads past 256 contribute nothing)
   int x = run;
 #pragma unroll
   for (int d = 1; d < 64; d <<= 1) {
     int y = __shfl_up(x, d, 64);
     if (lane >= d) x += y;
   }
-  if (lane == 63) wtot[wave] = x;
+  if (lane == 63 && wave < 4) wtot[wave] = x;
   __syncthreads();
-  int before = x - run;
-  for (int w = 0; w < wave; ++w) before += wtot[w];
+  if (tid < 256) {
+    int before = x - run;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) cum[tid * 4 + i] = before + v[i];
+    for (int i = 0; i < 4; ++i) cum[tid * 4 + i] = before + v[i];
+  }
   __syncthreads();
   return cum[g.E - 1];
 }
 
-template <int TM>
-__device__ void tile_locate(const GemmArgs &g, const int *cum, int mt, int &e, int &row0,
-                            int &row_end) {
+// Tile order inside one expert: its m-tiles are taken in groups of GM; a
+// group's tiles run n-tile by n-tile, and within an n-tile over the group's
+// m-tiles.  The m-tiles that read the same weight tile are therefore
+// neighbours in dispatch order (they start within moments of each other
+// and walk K in step, so the weights come from HBM once and from L2 for the
+// others), and the n-tiles that share a token tile are at most GM apart.
+// Tile t -> expert e, rows [row0, row_end) of its segment (row0 is the
+// first row of the m-tile), n-tile nt.
+template <int TM, int GM>
+__device__ void tile_locate(const GemmArgs &g, const int *cum, int ntn, int t, int &e, int &row0,
+                            int &row_end, int &nt) {
+  int first, mte, seg0, seg1;
   if (!g.offsets) {
     e = 0;
-    row0 = mt * TM;
-    row_end = g.rows;
-    return;
+    first = 0;
+    mte = (g.rows + TM - 1) / TM;
+    seg0 = 0;
+    seg1 = g.rows;
+  } else {
+    int lo = 0, hi = g.E - 1;
+    while (lo < hi) {
+      int mid = (lo + hi) >> 1;
+      if (cum[mid] * ntn > t) hi = mid;
+      else lo = mid + 1;
+    }
+    e = lo;
+    first = lo ? cum[lo - 1] : 0;
+    mte = cum[lo] - first;
+    seg0 = g.offsets[lo];
+    seg1 = g.offsets[lo + 1];
   }
-  int lo = 0, hi = g.E - 1;
-  while (lo < hi) {
-    int mid = (lo + hi) >> 1;
-    if (cum[mid] > mt) hi = mid;
-    else lo = mid + 1;
-  }
-  e = lo;
-  const int first = lo ? cum[lo - 1] : 0;
-  row0 = g.offsets[lo] + (mt - first) * TM;
-  row_end = g.offsets[lo + 1];
+  const int local = t - first * ntn;
+  const int grp = local / (GM * ntn), in = local - grp * (GM * ntn);
+  const int gsz = min(GM, mte - grp * GM);
+  nt = in / gsz;
+  row0 = seg0 + (grp * GM + in % gsz) * TM;
+  row_end = seg1;
 }
 
 // ----------------------------------------------------------------------------- tile
@@ -343,32 +390,34 @@ __device__ __forceinline__ int tslot(int r16, int g, int p) {
   return 16 * g + (r16 ^ ((2 * g + 8 * p) & 15));
 }
 
-// Workgroup tile: TN weight rows (NBT blocks) x TM tokens (MBT blocks).  Wave
-// w owns weight blocks [w*NBW, (w+1)*NBW) and all MBT token blocks.  Its
-// weight fragments come straight from global memory into registers (the
-// packed layout makes every wave access one contiguous KiB), one stage
-// ahead; the token tile, which all four waves share, is staged through LDS
-// (double-buffered, one barrier per stage).  A stage is half a K chunk: one
-// 128-byte line of each token row and two 1 KiB pieces of each weight block.
+// Workgroup tile: TN weight rows (NBT blocks) x TM tokens (MBT blocks), NWV
+// waves.  Wave w owns weight blocks [w*NBW, (w+1)*NBW) and all MBT token
+// blocks.  Its weight fragments come straight from global memory into
+// registers (the packed layout makes every wave access one contiguous KiB),
+// WPF stages ahead; the token tile, which all waves share, is staged through
+// LDS (double-buffered, one barrier per stage).  A stage is half a K chunk:
+// one 128-byte line of each token row and two 1 KiB pieces of each weight
+// block.  More waves per workgroup means fewer n-tiles per m-tile, so each
+// token tile is fetched fewer times.
 
-template <int F, int EPI, int OT, int TN, int TM, int WPF>
-__global__ __launch_bounds__(256, (WPF > 1 || (F == FMT_MX8 && TM > 64)) ? 1 : 2) void gemm_tile_kernel(GemmArgs g) {
+template <int F, int EPI, int OT, int TN, int TM, int NWV, int WPF, int OCC>
+__global__ __launch_bounds__(64 * NWV, OCC) void gemm_tile_kernel(GemmArgs g) {
+  constexpr int NTH = 64 * NWV;         // threads
   constexpr int NBT = TN / 16, MBT = TM / 16;
-  constexpr int NBW = NBT / 4;
+  constexpr int NBW = NBT / NWV;        // weight blocks per wave
   constexpr int TBYTES = MBT * 2048;    // token bytes per stage
-  constexpr int TLD = TM / 32;          // 16-byte token loads per thread per stage
-  static_assert(NBT % 4 == 0 && TLD >= 1, "tile shape");
+  constexpr int TLD = TM * 8 / NTH;     // 16-byte token loads per thread per stage
+  static_assert(NBT % NWV == 0 && TLD >= 1 && TLD * NTH == TM * 8, "tile shape");
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TBYTES];
   __shared__ int cum[1024];
   __shared__ uint8_t tscl[2][MBT * 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // Tile order: m-tile major, n-tile minor, so the n-tiles of one m-tile (which
-  // share its token rows) and the m-tiles of one expert (which share its
-  // weight tiles) run next to each other.  Workgroups are dealt round-robin
-  // to the 8 XCDs; each XCD takes one contiguous range of the actual tiles
-  // (counted on the device), so neighbours meet in the same L2 and the
-  // surplus workgroups of the upper-bound grid are spread over all XCDs.
+  // Tiles are numbered expert by expert in tile_locate's order.  Workgroups
+  // are dealt round-robin to the 8 XCDs; each XCD takes one contiguous range
+  // of the actual tiles (counted on the device), so neighbours meet in the
+  // same L2 and the surplus workgroups of the upper-bound grid are spread
+  // over all XCDs.
   const int ntn = g.N / TN;
   const int total = tile_scan<TM>(g, cum) * ntn;
 #if MOE_TILE_MAP == 0
@@ -380,42 +429,57 @@ __global__ __launch_bounds__(256, (WPF > 1 || (F == FMT_MX8 && TM > 64)) ? 1 : 2
   const int logical = blockIdx.x;
   if (logical >= total) return;
 #endif
-  const int mt = logical / ntn, nt = logical % ntn;
-  int e, row0, row_end;
-  tile_locate<TM>(g, cum, mt, e, row0, row_end);
+  int e, row0, row_end, nt;
+  tile_locate<TM, MOE_TILE_GM>(g, cum, ntn, logical, e, row0, row_end, nt);
 
   const int kcn = g.K / FmtInfo<F>::chunk_elems;
   const int nstage = 2 * kcn;
   const int nb0 = nt * NBT + wave * NBW;       // this wave's first weight block
-  const uint8_t *wsrc = g.w + (size_t)e * g.w_expert_stride + (size_t)nb0 * kcn * kBlockBytes +
-                        lane * 16;
-  const uint16_t *wss = nullptr;
-  if constexpr (F == FMT_MX8)
-    wss = g.w_scale + (size_t)e * g.ws_expert_stride + (size_t)nb0 * kcn * 64 + lane;
+  // Operands are read through buffer descriptors (base and size in scalar
+  // registers, 32-bit per-lane offsets): the per-stage address arithmetic is
+  // scalar and each lane keeps one offset per stream instead of a 64-bit
+  // pointer, which leaves the vector registers to the accumulators and the
+  // operands in flight.
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(g.w + (size_t)e * g.w_expert_stride,
+                                              (uint32_t)g.w_expert_stride);
+  const uint32_t wvoff = (uint32_t)(nb0 * kcn) * kBlockBytes + lane * 16;
+  const __amdgpu_buffer_rsrc_t trs = make_rsrc(g.a, (uint32_t)g.a_bytes);
+  // MX scales: weight scale pairs [row block][chunk][lane] of this expert,
+  // token scale bytes [row][K / 32]
+  __amdgpu_buffer_rsrc_t wsrs = wrs, tsrs = trs;
+  uint32_t wsvoff = 0;
+  if constexpr (F == FMT_MX8) {
+    wsrs = make_rsrc(g.w_scale + (size_t)e * g.ws_expert_stride,
+                     (uint32_t)(g.ws_expert_stride * sizeof(uint16_t)));
+    wsvoff = (uint32_t)((nb0 * kcn) * 64 + lane) * 2;
+    tsrs = make_rsrc(g.a_scale, (uint32_t)(g.a_bytes / g.a_row_bytes * (g.K / 32)));
+  }
 
   // this thread's token rows (fixed across stages)
-  const uint8_t *tsrc[TLD];
+  uint32_t tvoff[TLD];
   int tdst[TLD];
 #pragma unroll
   for (int i = 0; i < TLD; ++i) {
-    const int idx = tid + 256 * i;
+    const int idx = tid + NTH * i;
     const int rl = idx >> 3, seg = idx & 7;
     int r = row0 + rl;
     if (r >= row_end) r = row_end - 1;
-    tsrc[i] = g.a + token_of(g, r) * g.a_row_bytes + seg * 16;
+    tvoff[i] = (uint32_t)(token_of(g, r) * g.a_row_bytes) + seg * 16;
     tdst[i] = (rl >> 4) * 2048 + (seg >> 2) * 1024 + tslot(rl & 15, seg & 3, seg >> 2) * 16;
   }
-  // MX token scales: entry idx = tid + 256 i is (token block idx / 64, lane idx % 64)
-  constexpr int TSL = (F == FMT_MX8) ? (MBT * 64 + 255) / 256 : 1;
-  const uint8_t *tss[TSL];
+  // MX token scales: entry idx = tid + NTH i is (token block idx / 64, lane idx % 64)
+  constexpr int TSL = (F == FMT_MX8) ? (MBT * 64 + NTH - 1) / NTH : 1;
+  uint32_t tsvoff[TSL];
+#pragma unroll
+  for (int i = 0; i < TSL; ++i) tsvoff[i] = 0;
   if constexpr (F == FMT_MX8) {
 #pragma unroll
     for (int i = 0; i < TSL; ++i) {
-      const int idx = min(tid + 256 * i, MBT * 64 - 1);
+      const int idx = min(tid + NTH * i, MBT * 64 - 1);
       const int rl = (idx >> 6) * 16 + (idx & 15);
       int r = row0 + rl;
       if (r >= row_end) r = row_end - 1;
-      tss[i] = g.a_scale + token_of(g, r) * (g.K / 32) + ((idx >> 4) & 3);
+      tsvoff[i] = (uint32_t)(token_of(g, r) * (g.K / 32)) + ((idx >> 4) & 3);
     }
   }
 
@@ -424,10 +488,12 @@ __global__ __launch_bounds__(256, (WPF > 1 || (F == FMT_MX8 && TM > 64)) ? 1 : 2
   auto load_tokens = [&](int s) {
     const int kc = s >> 1, h = s & 1;
 #pragma unroll
-    for (int i = 0; i < TLD; ++i) treg[i] = *(const i32x4 *)(tsrc[i] + kc * 256 + h * 128);
+    for (int i = 0; i < TLD; ++i)
+      treg[i] = __builtin_amdgcn_raw_buffer_load_b128(trs, (int)tvoff[i], kc * 256 + h * 128, 0);
     if constexpr (F == FMT_MX8) {
 #pragma unroll
-      for (int i = 0; i < TSL; ++i) tsreg[i] = tss[i][8 * kc + 4 * h];
+      for (int i = 0; i < TSL; ++i)
+        tsreg[i] = __builtin_amdgcn_raw_buffer_load_b8(tsrs, (int)tsvoff[i], 8 * kc + 4 * h, 0);
     }
   };
   auto store_tokens = [&](int s) {
@@ -437,28 +503,27 @@ __global__ __launch_bounds__(256, (WPF > 1 || (F == FMT_MX8 && TM > 64)) ? 1 : 2
     if constexpr (F == FMT_MX8) {
 #pragma unroll
       for (int i = 0; i < TSL; ++i)
-        if (tid + 256 * i < MBT * 64) tscl[s & 1][tid + 256 * i] = (uint8_t)tsreg[i];
+        if (tid + NTH * i < MBT * 64) tscl[s & 1][tid + NTH * i] = (uint8_t)tsreg[i];
     }
   };
-  // weight fragments of WPF + 1 stages live in registers: stage s uses set
-  // s % (WPF + 1) while the loads of the next WPF stages are in flight
+  // NSET = WPF + 1 register sets of weight fragments: stage s multiplies
+  // one set while the loads of stages s + 1 .. s + WPF fill the others
   constexpr int NSET = WPF + 1;
-  i32x4 wr[NSET][NBW][2];
+  Frag<F> wr[NSET][NBW];
   uint32_t wsr[NSET][NBW];
   auto load_weights = [&](int s, int set) {
     const int kc = s >> 1, h = s & 1;
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
-      const uint8_t *p = wsrc + ((size_t)n * kcn + kc) * kBlockBytes + h * 2048;
-#pragma unroll
-      for (int q = 0; q < NSET; ++q)
-        if (q == set) {
-          wr[q][n][0] = *(const i32x4 *)p;
-          wr[q][n][1] = *(const i32x4 *)(p + 1024);
-          wsr[q][n] = 0;
-          if constexpr (F == FMT_MX8)
-            wsr[q][n] = (wss[((size_t)n * kcn + kc) * 64] >> (8 * h)) & 0xFFu;
-        }
+      const uint32_t so = (uint32_t)(n * kcn + kc) * kBlockBytes + h * 2048;
+      wr[set][n] = make_frag<F>(
+          __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)so, MOE_TILE_WAUX),
+          __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)(so + 1024), MOE_TILE_WAUX));
+      wsr[set][n] = 0;
+      if constexpr (F == FMT_MX8)
+        wsr[set][n] = (__builtin_amdgcn_raw_buffer_load_b16(wsrs, (int)wsvoff,
+                                                            (n * kcn + kc) * 128, 0) >>
+                       (8 * h)) & 0xFFu;
     }
   };
 
@@ -468,184 +533,72 @@ __global__ __launch_bounds__(256, (WPF > 1 || (F == FMT_MX8 && TM > 64)) ? 1 : 2
 #pragma unroll
     for (int m = 0; m < MBT; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // One stage.  Every load and LDS store is issued unconditionally (stage
+  // indices past the end are clamped to the last stage, whose data is then
+  // fetched again and never used): with no branches in the loop body the
+  // compiler counts the loads in flight exactly and waits only for the ones
+  // a step needs.  The order inside a stage is pinned with scheduling
+  // barriers: the next stage's weight loads go out first, so their latency
+  // is covered by this stage's matrix work; then the products; then the
+  // token tile of stage s + 1 moves from registers to LDS (its loads were
+  // issued a stage earlier) and the loads of stage s + 2 go out.  The LDS
+  // buffer written after the last stage is the one the stage before it
+  // read, which every wave has finished with at that stage's barrier.
   auto stage = [&](int s, int set) {
-    if (s + WPF < nstage) load_weights(s + WPF, (set + WPF) % NSET);
+    load_weights(min(s + WPF, nstage - 1), (set + WPF) % NSET);
+    __builtin_amdgcn_sched_barrier(0);
     const uint8_t *base = lds + (s & 1) * TBYTES;
+    // token fragments are read one token block ahead of the products that
+    // use them, so the LDS latency overlaps the matrix work
+    Frag<F> tf[2];
+    uint32_t tsf[2];
+    auto read_frag = [&](int m, int b) {
+      const uint8_t *p = base + m * 2048;
+      tf[b] = make_frag<F>(*(const i32x4 *)(p + tslot(lane & 15, lane >> 4, 0) * 16),
+                           *(const i32x4 *)(p + 1024 + tslot(lane & 15, lane >> 4, 1) * 16));
+      tsf[b] = 0;
+      if constexpr (F == FMT_MX8) tsf[b] = tscl[s & 1][m * 64 + lane];
+    };
+    read_frag(0, 0);
+#if MOE_TILE_SGB
+    if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#endif
 #pragma unroll
     for (int m = 0; m < MBT; ++m) {
-      const uint8_t *p = base + m * 2048;
-      const i32x4 t0 = *(const i32x4 *)(p + tslot(lane & 15, lane >> 4, 0) * 16);
-      const i32x4 t1 = *(const i32x4 *)(p + 1024 + tslot(lane & 15, lane >> 4, 1) * 16);
-      uint32_t ts = 0;
-      if constexpr (F == FMT_MX8) ts = tscl[s & 1][m * 64 + lane];
+      if (m + 1 < MBT) {
+        read_frag(m + 1, (m + 1) & 1);
+#if MOE_TILE_SGB
+        if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#endif
+      }
 #pragma unroll
-      for (int n = 0; n < NBW; ++n)
-#pragma unroll
-        for (int q = 0; q < NSET; ++q)
-          if (q == set) mfma_half<F>(acc[n][m], wr[q][n][0], wr[q][n][1], t0, t1, wsr[q][n], ts);
+      for (int n = 0; n < NBW; ++n) mfma_frag<F>(acc[n][m], wr[set][n], tf[m & 1], wsr[set][n], tsf[m & 1]);
+#if MOE_TILE_SGB
+      if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NBW, 0);
+#endif
     }
-    if (s + 1 < nstage) store_tokens(s + 1);
-    if (s + 2 < nstage) load_tokens(s + 2);
+    __builtin_amdgcn_sched_barrier(0);
+    store_tokens(s + 1);
+    load_tokens(min(s + 2, nstage - 1));
     __syncthreads();
   };
 
   load_tokens(0);
 #pragma unroll
-  for (int q = 0; q < WPF; ++q)
-    if (q < nstage) load_weights(q, q);
+  for (int q = 0; q < WPF; ++q) load_weights(min(q, nstage - 1), q);
   store_tokens(0);
-  if (nstage > 1) load_tokens(1);
+  load_tokens(min(1, nstage - 1));
   __syncthreads();
-
-  // the stage loop, unrolled by the number of register sets so every set
-  // index is a compile-time constant
-  for (int s0 = 0; s0 < nstage; s0 += NSET) {
+  // the loop takes NSET stages at a time so every register-set index is a
+  // compile-time constant; the remaining nstage % NSET stages follow it
+  int s0 = 0;
+  for (; s0 + NSET <= nstage; s0 += NSET) {
 #pragma unroll
-    for (int q = 0; q < NSET; ++q)
-      if (s0 + q < nstage) stage(s0 + q, q);
+    for (int q = 0; q < NSET; ++q) stage(s0 + q, q);
   }
-
 #pragma unroll
-  for (int m = 0; m < MBT; ++m) {
-    f32x4 col[NBW];
-#pragma unroll
-    for (int n = 0; n < NBW; ++n) col[n] = acc[n][m];
-    const int r = row0 + m * 16 + (lane & 15);
-    epilogue<EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane);
-  }
-}
-
-// ----------------------------------------------------------------------------- tile (LDS ring)
-// Same tile and wave roles as gemm_tile_kernel, but both operands reach LDS
-// through direct global->LDS loads (global_load_lds_dwordx4: each wave
-// instruction fills one contiguous KiB, lane l's 16 bytes at slot l) into a
-// ring of NS stages, so NS - 1 stages of loads are in flight while the
-// matrix cores work and no registers are tied up by them.  Each wave loads
-// its own weight pieces and a quarter of the token pieces.  Stage s is
-// consumed after this wave's loads for it have landed (vmcnt) and all waves
-// have met at a barrier (so the other waves' token pieces are in too); the
-// ring slot of stage s - 1 is refilled only after that barrier, once every
-// wave has finished reading it.  The barrier is the bare s_barrier with a
-// compiler memory clobber on each side: the ordering the pipeline needs is
-// given by the explicit waits, and a full workgroup fence would drain every
-// load in flight.
-
-#define MOE_GPTR(p) ((__attribute__((address_space(1))) void *)(p))
-#define MOE_LPTR(p) ((__attribute__((address_space(3))) void *)(p))
-
-// s_waitcnt with vmcnt(V) and lgkmcnt(0) (gfx9 encoding: vmcnt bits 3:0 and
-// 15:14, expcnt 6:4 left at its maximum, lgkmcnt 11:8)
-template <int V>
-__device__ __forceinline__ void wait_vm_lgkm0() {
-  static_assert(V >= 0 && V < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((V & 15) | ((V >> 4) << 14) | (7 << 4));
-}
-
-__device__ __forceinline__ void ring_barrier() {
-  __asm__ volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  __asm__ volatile("" ::: "memory");
-}
-
-template <int F, int EPI, int OT, int TN, int TM, int NS>
-__global__ __launch_bounds__(256, 1) void gemm_tile_dma_kernel(GemmArgs g) {
-  constexpr int NBT = TN / 16, MBT = TM / 16;
-  constexpr int NBW = NBT / 4;                 // weight blocks per wave
-  constexpr int WST = NBT * 2048, TST = MBT * 2048, STAGE = WST + TST;
-  constexpr int TPW = MBT * 2 / 4;             // token pieces loaded per wave per stage
-  constexpr int LPS = NBW * 2 + TPW;           // loads per wave per stage
-  static_assert(F != FMT_MX8, "MX uses gemm_tile_kernel");
-  static_assert(NBT % 4 == 0 && (MBT * 2) % 4 == 0 && NS >= 2, "tile shape");
-  static_assert((NS - 2) * LPS < 64, "vmcnt range");
-  extern __shared__ __attribute__((aligned(16))) uint8_t ring[];   // NS * STAGE
-  __shared__ int cum[1024];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int ntn = g.N / TN;
-  const int total = tile_scan<TM>(g, cum) * ntn;
-#if MOE_TILE_MAP == 0
-  const int per_xcd = (total + 7) >> 3;
-  const int local = blockIdx.x >> 3;
-  const int logical = (blockIdx.x & 7) * per_xcd + local;
-  if (local >= per_xcd || logical >= total) return;
-#else
-  const int logical = blockIdx.x;
-  if (logical >= total) return;
-#endif
-  const int mt = logical / ntn, nt = logical % ntn;
-  int e, row0, row_end;
-  tile_locate<TM>(g, cum, mt, e, row0, row_end);
-
-  const int kcn = g.K / FmtInfo<F>::chunk_elems;
-  const int nstage = 2 * kcn;
-  const int nb0 = nt * NBT + wave * NBW;
-  const uint8_t *wsrc = g.w + (size_t)e * g.w_expert_stride + (size_t)nb0 * kcn * kBlockBytes +
-                        lane * 16;
-  // token pieces this wave loads: q = wave * TPW + i -> block q / 2, piece q % 2
-  const uint8_t *tsrc[TPW];
-#pragma unroll
-  for (int i = 0; i < TPW; ++i) {
-    const int q = wave * TPW + i;
-    const int rl = (q >> 1) * 16 + (lane & 15);
-    int r = row0 + rl;
-    if (r >= row_end) r = row_end - 1;
-    tsrc[i] = g.a + token_of(g, r) * g.a_row_bytes + 64 * (q & 1) + 16 * (lane >> 4);
-  }
-
-  auto issue = [&](int s) {
-    const int kc = s >> 1, h = s & 1;
-    uint8_t *st = ring + (s % NS) * STAGE;
-#pragma unroll
-    for (int n = 0; n < NBW; ++n)
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-        __builtin_amdgcn_global_load_lds(
-            MOE_GPTR(wsrc + ((size_t)n * kcn + kc) * kBlockBytes + (2 * h + pp) * 1024),
-            MOE_LPTR(st + (wave * NBW + n) * 2048 + pp * 1024), 16, 0, 0);
-#pragma unroll
-    for (int i = 0; i < TPW; ++i) {
-      const int q = wave * TPW + i;
-      __builtin_amdgcn_global_load_lds(MOE_GPTR(tsrc[i] + kc * 256 + h * 128),
-                                       MOE_LPTR(st + WST + (q >> 1) * 2048 + (q & 1) * 1024),
-                                       16, 0, 0);
-    }
-  };
-
-  f32x4 acc[NBW][MBT];
-#pragma unroll
-  for (int n = 0; n < NBW; ++n)
-#pragma unroll
-    for (int m = 0; m < MBT; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int q = 0; q < NS - 1; ++q)
-    if (q < nstage) issue(q);
-
-  for (int s = 0; s < nstage; ++s) {
-    // this wave's loads for stage s are the oldest still counted: allow the
-    // later stages' loads (at most NS - 2 of them) to stay in flight
-    if (s + NS - 2 < nstage) wait_vm_lgkm0<(NS - 2) * LPS>();
-    else wait_vm_lgkm0<0>();
-    ring_barrier();
-    if (s + NS - 1 < nstage) issue(s + NS - 1);
-    const uint8_t *st = ring + (s % NS) * STAGE;
-    i32x4 wf[NBW][2], tf[MBT][2];
-#pragma unroll
-    for (int n = 0; n < NBW; ++n)
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-        wf[n][pp] = *(const i32x4 *)(st + (wave * NBW + n) * 2048 + pp * 1024 + lane * 16);
-#pragma unroll
-    for (int m = 0; m < MBT; ++m)
-#pragma unroll
-      for (int pp = 0; pp < 2; ++pp)
-        tf[m][pp] = *(const i32x4 *)(st + WST + m * 2048 + pp * 1024 + lane * 16);
-#pragma unroll
-    for (int m = 0; m < MBT; ++m)
-#pragma unroll
-      for (int n = 0; n < NBW; ++n)
-        mfma_half<F>(acc[n][m], wf[n][0], wf[n][1], tf[m][0], tf[m][1], 0, 0);
-  }
+  for (int q = 0; q < NSET - 1; ++q)
+    if (s0 + q < nstage) stage(s0 + q, q);
 
 #pragma unroll
   for (int m = 0; m < MBT; ++m) {
@@ -668,6 +621,25 @@ static hipError_t launch_skinny(const GemmArgs &g, int segs, hipStream_t stream)
   return hipGetLastError();
 }
 
+// Tiled kernel over the segments longer than g.split, NWV waves of 64
+// weight rows each.
+template <int F, int EPI, int OT, int NWV>
+static hipError_t launch_tile(GemmArgs g, int total_rows, hipStream_t stream) {
+  constexpr int TM = (F == FMT_MX8) ? MOE_TILE_TM_MX : MOE_TILE_TM;
+  constexpr int TN = 64 * NWV;
+  if (g.N % TN != 0) return hipErrorInvalidValue;
+  const int mtiles = g.offsets ? (total_rows + TM - 1) / TM + g.E : (g.rows + TM - 1) / TM;
+  g.mt_upper = mtiles;
+  // upper bound on the tiles, rounded up to whole rounds of the 8 XCDs
+  long long nblocks = (long long)mtiles * (g.N / TN);
+  nblocks = ((nblocks + 7) / 8) * 8 + 8;
+  constexpr int WPF = (F == FMT_MX8) ? 1 : MOE_TILE_WPF;
+  // two waves per SIMD
+  constexpr int OCC = (NWV >= 8) ? 1 : (F == FMT_MX8) ? MOE_TILE_OCC_MX : MOE_TILE_OCC;
+  gemm_tile_kernel<F, EPI, OT, TN, TM, NWV, WPF, OCC><<<(unsigned)nblocks, 64 * NWV, 0, stream>>>(g);
+  return hipGetLastError();
+}
+
 template <int F, int EPI, int OT>
 static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t stream) {
   GemmArgs g = g0;
@@ -677,6 +649,13 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
   // weight blocks a SwiGLU workgroup must hold: gate/up pairs (2), and for the
   // MX-quantising epilogue whole 32-column blocks (4)
   constexpr int NWS = (EPI == EPI_SWIGLU) ? (OT == FMT_MX8 ? 4 : 2) : 1;
+  // The tiled kernel addresses its operands with 32-bit offsets; beyond 4 GiB
+  // of token-side data or of one expert's weights every segment goes to the
+  // streaming kernel, which walks any number of rows in passes.
+  if (g.a_bytes > 0xFFFFFFFFll || g.w_expert_stride > 0xFFFFFFFFull) {
+    if (!g.offsets) return launch_skinny<F, EPI, OT, NWS, 4, 4>(g, 1, stream);
+    return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
+  }
   if (!g.offsets) {
     // one segment (shared expert): few weight blocks per workgroup, K split
     // over the four waves, so the weights spread over many workgroups
@@ -696,32 +675,9 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     hipError_t err = launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
     if (err != hipSuccess) return err;
   }
-  constexpr int TN = 256, TM = (F == FMT_MX8) ? MOE_TILE_TM_MX : 128;
-  if (g.N % TN != 0) return hipErrorInvalidValue;
-  const int mtiles = g.offsets ? (total_rows + TM - 1) / TM + g.E : (g.rows + TM - 1) / TM;
-  g.mt_upper = mtiles;
-  // upper bound on the tiles, rounded up to whole rounds of the 8 XCDs
-  long long nblocks = (long long)mtiles * (g.N / TN);
-  nblocks = ((nblocks + 7) / 8) * 8 + 8;
-#if MOE_TILE_DMA
-  if constexpr (F != FMT_MX8) {
-    constexpr int NS = 3;
-    const size_t lds = (size_t)NS * (TN / 16 + TM / 16) * 2048;
-    auto kern = gemm_tile_dma_kernel<F, EPI, OT, TN, TM, NS>;
-    static bool attr_set = false;
-    if (!attr_set) {
-      hipError_t err = hipFuncSetAttribute((const void *)kern,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-      if (err != hipSuccess) return err;
-      attr_set = true;
-    }
-    kern<<<(unsigned)nblocks, 256, lds, stream>>>(g);
-    return hipGetLastError();
-  }
-#endif
-  constexpr int WPF = (F == FMT_MX8) ? MOE_TILE_WPF_MX : 1;
-  gemm_tile_kernel<F, EPI, OT, TN, TM, WPF><<<(unsigned)nblocks, 256, 0, stream>>>(g);
-  return hipGetLastError();
+  constexpr int NWV = (F == FMT_MX8) ? 4 : MOE_TILE_NWV;
+  if (g.N % (64 * NWV) == 0) return launch_tile<F, EPI, OT, NWV>(g, total_rows, stream);
+  return launch_tile<F, EPI, OT, 4>(g, total_rows, stream);
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs &g, int fmt, int epi, int out_fmt, int total_rows,

@@ -96,6 +96,16 @@ __device__ __forceinline__ float mx_inv_scale(uint32_t s) {
   return __uint_as_float((uint32_t)(254 - (int)s) << 23);
 }
 
+// ----------------------------------------------------------------------------- buffer access
+
+// Raw buffer descriptor over [base, base + bytes) (stride 0, 32-bit data
+// format word of the gfx9 family).  Loads through it take a per-lane 32-bit
+// offset and a wave-uniform scalar offset.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // ----------------------------------------------------------------------------- wave helpers
 
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
@@ -132,6 +142,41 @@ __device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32
     const i32x8 b = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
     // operand format 0 = fp8 E4M3 for A and B; opsel 0 = scale byte 0
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, (int)ws, 0, (int)ts);
+  }
+}
+
+// One lane's operand for one half-chunk (pieces 2h and 2h + 1).  MX-fp8
+// keeps both pieces in one 8-register tuple, the operand its scaled
+// instruction reads, so nothing is copied between loading and multiplying.
+template <int F>
+struct Frag {
+  i32x4 p0, p1;
+};
+template <>
+struct Frag<FMT_MX8> {
+  i32x8 v;
+};
+
+template <int F>
+__device__ __forceinline__ Frag<F> make_frag(const i32x4 &a, const i32x4 &b) {
+  Frag<F> f;
+  if constexpr (F == FMT_MX8) {
+    f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else {
+    f.p0 = a;
+    f.p1 = b;
+  }
+  return f;
+}
+
+template <int F>
+__device__ __forceinline__ void mfma_frag(f32x4 &acc, const Frag<F> &w, const Frag<F> &t,
+                                          uint32_t ws, uint32_t ts) {
+  if constexpr (F == FMT_MX8) {
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.v, t.v, acc, 0, 0, 0, (int)ws, 0,
+                                                           (int)ts);
+  } else {
+    mfma_half<F>(acc, w.p0, w.p1, t.p0, t.p1, ws, ts);
   }
 }
 

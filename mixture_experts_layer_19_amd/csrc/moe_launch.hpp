@@ -17,6 +17,7 @@ struct GemmArgs {
   const uint8_t *a;           // token-side rows (x or h), row-major, expert format
   const uint8_t *a_scale;     // MX: [rows][K/32] E8M0 bytes
   long long a_row_bytes;      // bytes per token-side row
+  long long a_bytes;          // bytes of the whole token-side array
   const int32_t *sorted_src;  // row r reads token sorted_src[r] / k_route; NULL: row r
   int k_route;
   const int32_t *offsets;     // [E+1] segment bounds; NULL: one segment [0, rows)
