@@ -19,6 +19,9 @@
 //    stage.  The m-tile -> (expert, rows) map is computed on the device from
 //    the segment offsets, so no host synchronisation is needed; the grid is
 //    sized from an upper bound and surplus workgroups exit.
+#include <type_traits>
+#include <utility>
+
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
 
@@ -29,10 +32,16 @@
 #ifndef MOE_TILE_GM
 #define MOE_TILE_GM 8
 #endif
-// tiled kernel (f32 / bf16): token rows per tile, stages of weight
-// prefetch, workgroups per CU it is compiled for
-#ifndef MOE_TILE_TM
-#define MOE_TILE_TM 128
+// tiled kernel (f32 / bf16): WN x WM waves of 64 weight rows x MBW token
+// blocks, stages of weight prefetch, workgroups per CU for 4-wave groups
+#ifndef MOE_TILE_WN
+#define MOE_TILE_WN 4
+#endif
+#ifndef MOE_TILE_WM
+#define MOE_TILE_WM 1
+#endif
+#ifndef MOE_TILE_MBW
+#define MOE_TILE_MBW 8
 #endif
 #ifndef MOE_TILE_WPF
 #define MOE_TILE_WPF 1
@@ -40,11 +49,7 @@
 #ifndef MOE_TILE_OCC
 #define MOE_TILE_OCC 2
 #endif
-// waves per workgroup of the tiled kernel (64 weight rows each) and the
-// cache-policy bits of its weight loads
-#ifndef MOE_TILE_NWV
-#define MOE_TILE_NWV 4
-#endif
+// cache-policy bits of the weight loads
 #ifndef MOE_TILE_WAUX
 #define MOE_TILE_WAUX 0
 #endif
@@ -381,6 +386,16 @@ __device__ void tile_locate(const GemmArgs &g, const int *cum, int ntn, int t, i
 }
 
 // ----------------------------------------------------------------------------- tile
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{})
+template <typename Fn, int... Q>
+__device__ __forceinline__ void static_for_impl(Fn &&f, std::integer_sequence<int, Q...>) {
+  (f(std::integral_constant<int, Q>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
 // LDS slot of (row r16, lane group g) inside token piece p: the 16 slots of
 // a lane group are XOR-permuted so the stores of one wave (8 rows x 4 lane
 // groups x 2 pieces, 16 bytes each) fall into distinct banks, while a wave's
@@ -390,29 +405,39 @@ __device__ __forceinline__ int tslot(int r16, int g, int p) {
   return 16 * g + (r16 ^ ((2 * g + 8 * p) & 15));
 }
 
-// Workgroup tile: TN weight rows (NBT blocks) x TM tokens (MBT blocks), NWV
-// waves.  Wave w owns weight blocks [w*NBW, (w+1)*NBW) and all MBT token
-// blocks.  Its weight fragments come straight from global memory into
-// registers (the packed layout makes every wave access one contiguous KiB),
-// WPF stages ahead; the token tile, which all waves share, is staged through
-// LDS (double-buffered, one barrier per stage).  A stage is half a K chunk:
-// one 128-byte line of each token row and two 1 KiB pieces of each weight
-// block.  More waves per workgroup means fewer n-tiles per m-tile, so each
-// token tile is fetched fewer times.
+// Workgroup tile: TN = 64 WN weight rows (NBT blocks) x TM = 16 WM MBW tokens
+// (MBT blocks), WN x WM waves.  Wave (wn, wm) owns weight blocks
+// [wn*NBW, (wn+1)*NBW) and token blocks [wm*MBW, (wm+1)*MBW).  Its weight
+// fragments come straight from global memory into registers (the packed
+// layout makes every wave access one contiguous KiB), WPF stages ahead; with
+// WM = 2 the two waves of a weight slice load the same lines at the same
+// stage, so the second load is served by the CU's L1 and the L2 sees each
+// weight byte once per tile.  The token tile is staged through LDS
+// (double-buffered, one barrier per stage).  A stage is half a K chunk: one
+// 128-byte line of each token row and two 1 KiB pieces of each weight block.
+// Larger tiles fetch fewer bytes from L2 per multiply-add: TN-wide tiles
+// fetch each token tile N / TN times, TM-tall tiles each weight tile M / TM
+// times.
 
-template <int F, int EPI, int OT, int TN, int TM, int NWV, int WPF, int OCC>
-__global__ __launch_bounds__(64 * NWV, OCC) void gemm_tile_kernel(GemmArgs g) {
+template <int F, int EPI, int OT, int WN, int WM, int MBW, int WPF, int OCC>
+__global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g) {
+  constexpr int NWV = WN * WM;
   constexpr int NTH = 64 * NWV;         // threads
+  constexpr int TN = 64 * WN, TM = 16 * WM * MBW;
   constexpr int NBT = TN / 16, MBT = TM / 16;
-  constexpr int NBW = NBT / NWV;        // weight blocks per wave
+  constexpr int NBW = 4;                // weight blocks per wave
   constexpr int TBYTES = MBT * 2048;    // token bytes per stage
   constexpr int TLD = TM * 8 / NTH;     // 16-byte token loads per thread per stage
-  static_assert(NBT % NWV == 0 && TLD >= 1 && TLD * NTH == TM * 8, "tile shape");
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2 * TBYTES];
+  static_assert(TLD >= 1 && TLD * NTH == TM * 8, "tile shape");
+  // token tile: two LDS slots, one array each
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[TBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[TBYTES];
+  auto tbuf = [&](int slot) -> uint8_t * { return slot == 0 ? tb0 : tb1; };
   __shared__ int cum[1024];
   __shared__ uint8_t tscl[2][MBT * 64];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave % WN, wm = wave / WN;
   // Tiles are numbered expert by expert in tile_locate's order.  Workgroups
   // are dealt round-robin to the 8 XCDs; each XCD takes one contiguous range
   // of the actual tiles (counted on the device), so neighbours meet in the
@@ -434,7 +459,7 @@ __global__ __launch_bounds__(64 * NWV, OCC) void gemm_tile_kernel(GemmArgs g) {
 
   const int kcn = g.K / FmtInfo<F>::chunk_elems;
   const int nstage = 2 * kcn;
-  const int nb0 = nt * NBT + wave * NBW;       // this wave's first weight block
+  const int nb0 = nt * NBT + wn * NBW;         // this wave's first weight block
   // Operands are read through buffer descriptors (base and size in scalar
   // registers, 32-bit per-lane offsets): the per-stage address arithmetic is
   // scalar and each lane keeps one offset per stream instead of a 64-bit
@@ -497,13 +522,16 @@ __global__ __launch_bounds__(64 * NWV, OCC) void gemm_tile_kernel(GemmArgs g) {
     }
   };
   auto store_tokens = [&](int s) {
-    uint8_t *base = lds + (s & 1) * TBYTES;
+    uint8_t *base = tbuf(s & 1);
 #pragma unroll
     for (int i = 0; i < TLD; ++i) *(i32x4 *)(base + tdst[i]) = treg[i];
     if constexpr (F == FMT_MX8) {
 #pragma unroll
       for (int i = 0; i < TSL; ++i)
-        if (tid + NTH * i < MBT * 64) tscl[s & 1][tid + NTH * i] = (uint8_t)tsreg[i];
+        // (a runtime test only for a partial last round: a branch here would
+        // split the stage into several blocks for the scheduler)
+        if ((i + 1) * NTH <= MBT * 64 || tid + NTH * i < MBT * 64)
+          tscl[s & 1][tid + NTH * i] = (uint8_t)tsreg[i];
     }
   };
   // NSET = WPF + 1 register sets of weight fragments: stage s multiplies
@@ -527,11 +555,11 @@ __global__ __launch_bounds__(64 * NWV, OCC) void gemm_tile_kernel(GemmArgs g) {
     }
   };
 
-  f32x4 acc[NBW][MBT];
+  f32x4 acc[NBW][MBW];
 #pragma unroll
   for (int n = 0; n < NBW; ++n)
 #pragma unroll
-    for (int m = 0; m < MBT; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < MBW; ++m) acc[n][m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // One stage.  Every load and LDS store is issued unconditionally (stage
   // indices past the end are clamped to the last stage, whose data is then
@@ -544,10 +572,13 @@ __global__ __launch_bounds__(64 * NWV, OCC) void gemm_tile_kernel(GemmArgs g) {
   // issued a stage earlier) and the loads of stage s + 2 go out.  The LDS
   // buffer written after the last stage is the one the stage before it
   // read, which every wave has finished with at that stage's barrier.
-  auto stage = [&](int s, int set) {
+  // One stage: set and slot (the register set of its weights, the LDS slot
+  // of its tokens) are compile-time constants.
+  auto stage = [&](int s, auto set_c, auto slot_c) {
+    constexpr int set = decltype(set_c)::value, slot = decltype(slot_c)::value;
     load_weights(min(s + WPF, nstage - 1), (set + WPF) % NSET);
     __builtin_amdgcn_sched_barrier(0);
-    const uint8_t *base = lds + (s & 1) * TBYTES;
+    const uint8_t *base = tbuf(slot) + wm * MBW * 2048;
     // token fragments are read one token block ahead of the products that
     // use them, so the LDS latency overlaps the matrix work
     Frag<F> tf[2];
@@ -557,22 +588,23 @@ __global__ __launch_bounds__(64 * NWV, OCC) void gemm_tile_kernel(GemmArgs g) {
       tf[b] = make_frag<F>(*(const i32x4 *)(p + tslot(lane & 15, lane >> 4, 0) * 16),
                            *(const i32x4 *)(p + 1024 + tslot(lane & 15, lane >> 4, 1) * 16));
       tsf[b] = 0;
-      if constexpr (F == FMT_MX8) tsf[b] = tscl[s & 1][m * 64 + lane];
+      if constexpr (F == FMT_MX8) tsf[b] = tscl[slot][(wm * MBW + m) * 64 + lane];
     };
     read_frag(0, 0);
 #if MOE_TILE_SGB
     if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #endif
 #pragma unroll
-    for (int m = 0; m < MBT; ++m) {
-      if (m + 1 < MBT) {
+    for (int m = 0; m < MBW; ++m) {
+      if (m + 1 < MBW) {
         read_frag(m + 1, (m + 1) & 1);
 #if MOE_TILE_SGB
         if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
 #endif
       }
 #pragma unroll
-      for (int n = 0; n < NBW; ++n) mfma_frag<F>(acc[n][m], wr[set][n], tf[m & 1], wsr[set][n], tsf[m & 1]);
+      for (int n = 0; n < NBW; ++n)
+        mfma_frag<F>(acc[n][m], wr[set][n], tf[m & 1], wsr[set][n], tsf[m & 1]);
 #if MOE_TILE_SGB
       if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NBW, 0);
 #endif
@@ -582,30 +614,31 @@ __global__ __launch_bounds__(64 * NWV, OCC) void gemm_tile_kernel(GemmArgs g) {
     load_tokens(min(s + 2, nstage - 1));
     __syncthreads();
   };
-
   load_tokens(0);
 #pragma unroll
   for (int q = 0; q < WPF; ++q) load_weights(min(q, nstage - 1), q);
   store_tokens(0);
   load_tokens(min(1, nstage - 1));
   __syncthreads();
-  // the loop takes NSET stages at a time so every register-set index is a
-  // compile-time constant; the remaining nstage % NSET stages follow it
+  // stages in periods of P = lcm(NSET, 2) (slot = s % 2) so that set and
+  // slot are constants; the last nstage % P stages follow the loop
+  constexpr int P = (NSET % 2 == 0) ? NSET : 2 * NSET;
+  auto stage_q = [&](int s, auto q) {
+    constexpr int Q = decltype(q)::value;
+    stage(s, std::integral_constant<int, Q % NSET>{}, std::integral_constant<int, Q % 2>{});
+  };
   int s0 = 0;
-  for (; s0 + NSET <= nstage; s0 += NSET) {
-#pragma unroll
-    for (int q = 0; q < NSET; ++q) stage(s0 + q, q);
-  }
-#pragma unroll
-  for (int q = 0; q < NSET - 1; ++q)
-    if (s0 + q < nstage) stage(s0 + q, q);
+  for (; s0 + P <= nstage; s0 += P) static_for<P>([&](auto q) { stage_q(s0 + q.value, q); });
+  static_for<P - 1>([&](auto q) {
+    if (s0 + q.value < nstage) stage_q(s0 + q.value, q);
+  });
 
 #pragma unroll
-  for (int m = 0; m < MBT; ++m) {
+  for (int m = 0; m < MBW; ++m) {
     f32x4 col[NBW];
 #pragma unroll
     for (int n = 0; n < NBW; ++n) col[n] = acc[n][m];
-    const int r = row0 + m * 16 + (lane & 15);
+    const int r = row0 + (wm * MBW + m) * 16 + (lane & 15);
     epilogue<EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane);
   }
 }
@@ -621,22 +654,19 @@ static hipError_t launch_skinny(const GemmArgs &g, int segs, hipStream_t stream)
   return hipGetLastError();
 }
 
-// Tiled kernel over the segments longer than g.split, NWV waves of 64
-// weight rows each.
-template <int F, int EPI, int OT, int NWV>
+// Tiled kernel over the segments longer than g.split: WN x WM waves, MBW
+// token blocks per wave.
+template <int F, int EPI, int OT, int WN, int WM, int MBW, int WPF, int OCC>
 static hipError_t launch_tile(GemmArgs g, int total_rows, hipStream_t stream) {
-  constexpr int TM = (F == FMT_MX8) ? MOE_TILE_TM_MX : MOE_TILE_TM;
-  constexpr int TN = 64 * NWV;
+  constexpr int TN = 64 * WN, TM = 16 * WM * MBW;
   if (g.N % TN != 0) return hipErrorInvalidValue;
   const int mtiles = g.offsets ? (total_rows + TM - 1) / TM + g.E : (g.rows + TM - 1) / TM;
   g.mt_upper = mtiles;
   // upper bound on the tiles, rounded up to whole rounds of the 8 XCDs
   long long nblocks = (long long)mtiles * (g.N / TN);
   nblocks = ((nblocks + 7) / 8) * 8 + 8;
-  constexpr int WPF = (F == FMT_MX8) ? 1 : MOE_TILE_WPF;
-  // two waves per SIMD
-  constexpr int OCC = (NWV >= 8) ? 1 : (F == FMT_MX8) ? MOE_TILE_OCC_MX : MOE_TILE_OCC;
-  gemm_tile_kernel<F, EPI, OT, TN, TM, NWV, WPF, OCC><<<(unsigned)nblocks, 64 * NWV, 0, stream>>>(g);
+  gemm_tile_kernel<F, EPI, OT, WN, WM, MBW, WPF, OCC>
+      <<<(unsigned)nblocks, 64 * WN * WM, 0, stream>>>(g);
   return hipGetLastError();
 }
 
@@ -675,9 +705,18 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     hipError_t err = launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
     if (err != hipSuccess) return err;
   }
-  constexpr int NWV = (F == FMT_MX8) ? 4 : MOE_TILE_NWV;
-  if (g.N % (64 * NWV) == 0) return launch_tile<F, EPI, OT, NWV>(g, total_rows, stream);
-  return launch_tile<F, EPI, OT, 4>(g, total_rows, stream);
+  if constexpr (F == FMT_MX8) {
+    return launch_tile<F, EPI, OT, 4, 1, MOE_TILE_TM_MX / 16, 1, MOE_TILE_OCC_MX>(g, total_rows,
+                                                                                  stream);
+  } else {
+    // two waves per SIMD: one workgroup of WN x WM = 8 waves, or two of 4
+    constexpr int WN = MOE_TILE_WN, WM = MOE_TILE_WM;
+    constexpr int OCC = (WN * WM >= 8) ? 1 : MOE_TILE_OCC;
+    if (g.N % (64 * WN) == 0)
+      return launch_tile<F, EPI, OT, WN, WM, MOE_TILE_MBW, MOE_TILE_WPF, OCC>(g, total_rows,
+                                                                               stream);
+    return launch_tile<F, EPI, OT, 4, 1, 8, 1, 2>(g, total_rows, stream);
+  }
 }
 
 hipError_t launch_grouped_gemm(const GemmArgs &g, int fmt, int epi, int out_fmt, int total_rows,
