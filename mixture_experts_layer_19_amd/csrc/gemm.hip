@@ -19,9 +19,6 @@
 //    stage.  The m-tile -> (expert, rows) map is computed on the device from
 //    the segment offsets, so no host synchronisation is needed; the grid is
 //    sized from an upper bound and surplus workgroups exit.
-#include <type_traits>
-#include <utility>
-
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
 
@@ -386,24 +383,7 @@ __device__ void tile_locate(const GemmArgs &g, const int *cum, int ntn, int t, i
 }
 
 // ----------------------------------------------------------------------------- tile
-// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{})
-template <typename Fn, int... Q>
-__device__ __forceinline__ void static_for_impl(Fn &&f, std::integer_sequence<int, Q...>) {
-  (f(std::integral_constant<int, Q>{}), ...);
-}
-template <int N, typename Fn>
-__device__ __forceinline__ void static_for(Fn &&f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>{});
-}
 
-// LDS slot of (row r16, lane group g) inside token piece p: the 16 slots of
-// a lane group are XOR-permuted so the stores of one wave (8 rows x 4 lane
-// groups x 2 pieces, 16 bytes each) fall into distinct banks, while a wave's
-// fragment read (lane group g reads slots 16 g .. 16 g + 15) stays
-// conflict-free.
-__device__ __forceinline__ int tslot(int r16, int g, int p) {
-  return 16 * g + (r16 ^ ((2 * g + 8 * p) & 15));
-}
 
 // Workgroup tile: TN = 64 WN weight rows (NBT blocks) x TM = 16 WM MBW tokens
 // (MBT blocks), WN x WM waves.  Wave (wn, wm) owns weight blocks

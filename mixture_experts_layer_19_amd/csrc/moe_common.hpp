@@ -34,6 +34,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 namespace moe {
 
 constexpr int kChunkBytes = 256;      // bytes of one row per K chunk
@@ -108,6 +111,17 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 // ----------------------------------------------------------------------------- wave helpers
 
+// f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{})
+template <typename Fn, int... Q>
+__device__ __forceinline__ void static_for_impl(Fn &&f, std::integer_sequence<int, Q...>) {
+  (f(std::integral_constant<int, Q>{}), ...);
+}
+template <int N, typename Fn>
+__device__ __forceinline__ void static_for(Fn &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+
 __device__ __forceinline__ float wave_max_xor(float v, int mask) {
   return fmaxf(v, __shfl_xor(v, mask, 64));
 }
@@ -115,6 +129,16 @@ __device__ __forceinline__ float wave_max_xor(float v, int mask) {
 // ----------------------------------------------------------------------------- MFMA
 
 __device__ __forceinline__ int chunk_off(int g, int p) { return 128 * (p >> 1) + 64 * (p & 1) + 16 * g; }
+
+// LDS slot of (row r16, lane group g) inside a staged token piece p (0 or 1
+// within a half-chunk): the 16 slots of
+// a lane group are XOR-permuted so the stores of one wave (8 rows x 4 lane
+// groups x 2 pieces, 16 bytes each) fall into distinct banks, while a wave's
+// fragment read (lane group g reads slots 16 g .. 16 g + 15) stays
+// conflict-free.
+__device__ __forceinline__ int tslot(int r16, int g, int p) {
+  return 16 * g + (r16 ^ ((2 * g + 8 * p) & 15));
+}
 
 // acc += W x T over one half-chunk.  w0, w1 / t0, t1: the lane's two
 // 16-byte pieces of this half (pieces 2h and 2h + 1).  ws, ts: E8M0 scale

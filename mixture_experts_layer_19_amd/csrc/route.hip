@@ -90,78 +90,194 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT *__restrict
   }
 }
 
-// bf16 activations: matrix-core kernel.  W_r is split exactly into three
+// bf16 activations: matrix-core kernels.  W_r is split exactly into three
 // bf16 terms, w = hi + mid + lo (each remainder is exact in fp32 and the last
 // holds at most 8 significant bits), so x . w = x . hi + x . mid + x . lo
 // with every product exact in fp32; three bf16 MFMAs per step accumulate the
-// sum in fp32.  Fragment layout as in moe_common.hpp with 128-element
-// chunks: W_r rows are the A operand (lane row = expert), x rows the B
-// operand (lane column = token).  Grid: (token tiles of 16*MBW, expert
-// tiles of 64 = 4 waves x 16, K slices of KL).
+// sum in fp32.  The split is done once per call by router_split_kernel into
+// fragment order; router_gemm_kernel then only loads and multiplies.
+//
+// Fragment layout as in moe_common.hpp: W_r rows are the A operand (lane
+// row = expert), x rows the B operand (lane column = token).  A stage is 64
+// K elements (half a 128-element chunk); in stage s lane (g, r) holds, for
+// piece pp = 0, 1, the 8 elements from K = 64 s + 32 pp + 8 g.  The split
+// weights are stored [term][expert block][stage][pp][lane][8 bf16], so one
+// wave-wide 16-byte load reads a contiguous KiB.
 
-__device__ __forceinline__ void split_bf16x3(const float (&v)[8], bf16x8 &hi, bf16x8 &mid,
-                                             bf16x8 &lo) {
+__device__ __forceinline__ void split_bf16x3(const float (&v)[8], uint16_t (&hi)[8],
+                                             uint16_t (&mid)[8], uint16_t (&lo)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const uint16_t h = f32_to_bf16_rne(v[i]);
     const float r = v[i] - bf16_to_f32(h);
     const uint16_t m = f32_to_bf16_rne(r);
     const float r2 = r - bf16_to_f32(m);
-    const uint16_t l = f32_to_bf16_rne(r2);
-    hi[i] = __builtin_bit_cast(__bf16, h);
-    mid[i] = __builtin_bit_cast(__bf16, m);
-    lo[i] = __builtin_bit_cast(__bf16, l);
+    hi[i] = h;
+    mid[i] = m;
+    lo[i] = f32_to_bf16_rne(r2);
   }
 }
 
-template <int MBW>
-__global__ __launch_bounds__(256) void router_mfma_kernel(const uint16_t *__restrict__ x,
-                                                          const float *__restrict__ Wr,
-                                                          float *__restrict__ part, int T, int H,
-                                                          int E, int KL) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, r = lane & 15;
-  const int t0 = blockIdx.x * 16 * MBW;
-  const int e0 = blockIdx.y * 64 + wave * 16;
-  const int ks = blockIdx.z;
-  const int ea = e0 + r;
-  const float *wrow = Wr + (size_t)(ea < E ? ea : E - 1) * H;
-  const uint16_t *xrow[MBW];
+// One thread per (expert block, stage, pp, lane); experts past E are zero.
+__global__ __launch_bounds__(256) void router_split_kernel(const float *__restrict__ Wr, int E,
+                                                           int H, int EB, uint4 *__restrict__ out) {
+  const int nst = H / 64;
+  const long long per_term = (long long)EB * nst * 2 * 64;
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= per_term) return;
+  const int lane = (int)(i & 63), pp = (int)((i >> 6) & 1);
+  const long long q = i >> 7;
+  const int st = (int)(q % nst), eb = (int)(q / nst);
+  const int e = eb * 16 + (lane & 15), k0 = 64 * st + 32 * pp + 8 * (lane >> 4);
+  float v[8];
+  if (e < E) {
+    const float4 a = *(const float4 *)(Wr + (size_t)e * H + k0);
+    const float4 b = *(const float4 *)(Wr + (size_t)e * H + k0 + 4);
+    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
+    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+  } else {
 #pragma unroll
-  for (int m = 0; m < MBW; ++m) {
-    int t = t0 + 16 * m + r;
-    xrow[m] = x + (size_t)(t < T ? t : T - 1) * H;
+    for (int j = 0; j < 8; ++j) v[j] = 0.0f;
   }
-  f32x4 acc[MBW];
+  uint16_t t[3][8];
+  split_bf16x3(v, t[0], t[1], t[2]);
 #pragma unroll
-  for (int m = 0; m < MBW; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const int kend = (ks + 1) * KL;
-  for (int kc = ks * KL; kc < kend; kc += 128) {
+  for (int term = 0; term < 3; ++term) {
+    uint4 o;
+    o.x = (uint32_t)t[term][0] | ((uint32_t)t[term][1] << 16);
+    o.y = (uint32_t)t[term][2] | ((uint32_t)t[term][3] << 16);
+    o.z = (uint32_t)t[term][4] | ((uint32_t)t[term][5] << 16);
+    o.w = (uint32_t)t[term][6] | ((uint32_t)t[term][7] << 16);
+    out[term * per_term + i] = o;
+  }
+}
+
+// Workgroup: 4 waves, 16 MBT tokens x 64 experts; wave w takes expert block
+// w of the workgroup's range and all MBT token blocks.  The token tile (one
+// 128-byte line per row and stage) is staged through LDS, double-buffered,
+// with the same slot permutation as the expert GEMM; the split weights go
+// from global memory into registers WPF stages ahead.  The work per loaded
+// byte is small, so latency is hidden by depth and by many resident waves
+// (few registers per wave).
+//
+// Work order: K slice major, then token tile, then expert tile.  The 1-D
+// grid is dealt round-robin to the 8 XCDs and each XCD takes one contiguous
+// range of that order, so an XCD's L2 holds the split weights of one or two
+// K slices while the expert tiles that share a token tile run side by side.
+template <int MBT, int WPF>
+__global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
+                                                          const uint4 *__restrict__ wsplit,
+                                                          float *__restrict__ part, int T, int H,
+                                                          int E, int EB, int nsl, int n_et,
+                                                          int n_tt, int ksn) {
+  constexpr int TBYTES = MBT * 2048;
+  constexpr int TLD = MBT * 16 * 8 / 256;   // 16-byte token loads per thread per stage
+  constexpr int NSET = WPF + 1;
+  static_assert(TLD >= 1, "tile shape");
+  __shared__ __attribute__((aligned(16))) uint8_t tb0[TBYTES];
+  __shared__ __attribute__((aligned(16))) uint8_t tb1[TBYTES];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int total = n_et * n_tt * ksn, per_xcd = (total + 7) >> 3;
+  const int logical = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if ((int)(blockIdx.x >> 3) >= per_xcd || logical >= total) return;
+  const int et = logical % n_et, tt = (logical / n_et) % n_tt, ks = logical / (n_et * n_tt);
+  const int t0 = tt * 16 * MBT;
+  const int eb = min(et * 4 + wave, EB - 1);   // loads; stores test the real block
+  const bool eb_ok = et * 4 + wave < EB;
+  const int nst = H / 64, s_begin = ks * nsl;
+  const int s_end = min(nst, s_begin + nsl);
+  if (s_begin >= nst) return;
+  const long long per_term = (long long)EB * nst * 2 * 64;
+  const uint4 *wbase = wsplit + (long long)eb * nst * 128 + lane;
+
+  // token rows of this thread (clamped into [0, T))
+  const uint8_t *tsrc[TLD];
+  int tdst[TLD];
 #pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      const int off = kc + chunk_off(g, p) / 2;
-      const float4 w0 = *(const float4 *)(wrow + off);
-      const float4 w1 = *(const float4 *)(wrow + off + 4);
-      const float v[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-      bf16x8 hi, mid, lo;
-      split_bf16x3(v, hi, mid, lo);
+  for (int i = 0; i < TLD; ++i) {
+    const int idx = tid + 256 * i, rl = idx >> 3, seg = idx & 7;
+    const int t = min(t0 + rl, T - 1);
+    tsrc[i] = (const uint8_t *)(x + (size_t)t * H) + seg * 16;
+    tdst[i] = (rl >> 4) * 2048 + (seg >> 2) * 1024 + tslot(rl & 15, seg & 3, seg >> 2) * 16;
+  }
+  i32x4 treg[TLD];
+  auto load_tokens = [&](int s) {
 #pragma unroll
-      for (int m = 0; m < MBW; ++m) {
-        const bf16x8 b = *(const bf16x8 *)(xrow[m] + off);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(hi, b, acc[m], 0, 0, 0);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(mid, b, acc[m], 0, 0, 0);
-        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(lo, b, acc[m], 0, 0, 0);
+    for (int i = 0; i < TLD; ++i) treg[i] = *(const i32x4 *)(tsrc[i] + s * 128);
+  };
+  auto store_tokens = [&](uint8_t *buf) {
+#pragma unroll
+    for (int i = 0; i < TLD; ++i) *(i32x4 *)(buf + tdst[i]) = treg[i];
+  };
+  // weight fragments of one stage: [term][pp]
+  i32x4 wr[NSET][3][2];
+  auto load_weights = [&](int s, int set) {
+#pragma unroll
+    for (int term = 0; term < 3; ++term)
+#pragma unroll
+      for (int pp = 0; pp < 2; ++pp) {
+        const uint4 v = wbase[term * per_term + (long long)s * 128 + pp * 64];
+#pragma unroll
+        for (int q = 0; q < NSET; ++q)
+          if (q == set) wr[q][term][pp] = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+      }
+  };
+  f32x4 acc[MBT];
+#pragma unroll
+  for (int m = 0; m < MBT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // stage s: weights in register set `set`, tokens in LDS slot `slot`
+  auto stage = [&](int s, auto set_c, auto slot_c) {
+    constexpr int set = decltype(set_c)::value, slot = decltype(slot_c)::value;
+    load_weights(min(s + WPF, s_end - 1), (set + WPF) % NSET);
+    const uint8_t *base = slot ? tb1 : tb0;
+#pragma unroll
+    for (int m = 0; m < MBT; ++m) {
+      const uint8_t *p = base + m * 2048;
+      const i32x4 b0 = *(const i32x4 *)(p + tslot(lane & 15, lane >> 4, 0) * 16);
+      const i32x4 b1 = *(const i32x4 *)(p + 1024 + tslot(lane & 15, lane >> 4, 1) * 16);
+#pragma unroll
+      for (int term = 0; term < 3; ++term) {
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, wr[set][term][0]), __builtin_bit_cast(bf16x8, b0), acc[m],
+            0, 0, 0);
+        acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, wr[set][term][1]), __builtin_bit_cast(bf16x8, b1), acc[m],
+            0, 0, 0);
       }
     }
-  }
-  // accumulator: expert e0 + 4 g + i, token t0 + 16 m + r
+    store_tokens(slot ? tb0 : tb1);
+    load_tokens(min(s + 2, s_end - 1));
+    __syncthreads();
+  };
+
+  load_tokens(s_begin);
 #pragma unroll
-  for (int m = 0; m < MBW; ++m) {
+  for (int q = 0; q < WPF; ++q) load_weights(min(s_begin + q, s_end - 1), q);
+  store_tokens(tb0);
+  load_tokens(min(s_begin + 1, s_end - 1));
+  __syncthreads();
+  // periods of P = lcm(NSET, 2) stages keep set and slot compile-time
+  constexpr int P = (NSET % 2 == 0) ? NSET : 2 * NSET;
+  auto stage_q = [&](int s, auto q) {
+    constexpr int Q = decltype(q)::value;
+    stage(s, std::integral_constant<int, Q % NSET>{}, std::integral_constant<int, Q % 2>{});
+  };
+  int s = s_begin;
+  for (; s + P <= s_end; s += P) static_for<P>([&](auto q) { stage_q(s + q.value, q); });
+  static_for<P - 1>([&](auto q) {
+    if (s + q.value < s_end) stage_q(s + q.value, q);
+  });
+
+  // accumulator: expert 16 eb + 4 g + i, token t0 + 16 m + r
+  const int g = lane >> 4, r = lane & 15;
+#pragma unroll
+  for (int m = 0; m < MBT; ++m) {
     const int t = t0 + 16 * m + r;
-    if (t >= T) continue;
+    if (t >= T || !eb_ok) continue;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = e0 + 4 * g + i;
+      const int e = 16 * eb + 4 * g + i;
       if (e < E) part[((size_t)ks * T + t) * E + e] = acc[m][i];
     }
   }
@@ -194,8 +310,20 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   for (int i = 0; i < NPL; ++i) {
     int e = lane + 64 * i;
     if (e < E) {
+      // the slices in order, four loads in flight at a time
+      const float *pe = part + (size_t)t * E + e;
+      const size_t stride = (size_t)T * E;
       double zd = bias ? (double)bias[e] : 0.0;
-      for (int ks = 0; ks < ksn; ++ks) zd += (double)part[((size_t)ks * T + t) * E + e];
+      int ks = 0;
+      for (; ks + 4 <= ksn; ks += 4) {
+        const float a0 = pe[ks * stride], a1 = pe[(ks + 1) * stride];
+        const float a2 = pe[(ks + 2) * stride], a3 = pe[(ks + 3) * stride];
+        zd += (double)a0;
+        zd += (double)a1;
+        zd += (double)a2;
+        zd += (double)a3;
+      }
+      for (; ks < ksn; ++ks) zd += (double)pe[ks * stride];
       const float z = (float)zd;
       s[i] = (float)(1.0 / (1.0 + exp(-(double)z)));
     } else {
@@ -234,20 +362,41 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   }
 }
 
-// K slices of the bf16 logit kernel: short fp32 partials for small batches
-// (which also spreads the few token tiles over many workgroups), long ones
-// for large batches.
-static void router_plan(int T, int H, int x_is_bf16, int &ksn, int &kl) {
-  if (!x_is_bf16) { ksn = 1; kl = H; return; }
-  kl = (T <= 256) ? 256 : 2048;
-  if (H % kl) kl = 128;
-  ksn = H / kl;
+// Partial-sum slices of the logits.  fp32 activations: one.  bf16: enough K
+// slices (of whole 64-element stages, a power of two dividing H / 64) that
+// the grid holds about 256 workgroups or more.
+struct RoutePlan {
+  int ebw, mbt, ksn, nsl, eb;
+};
+
+static RoutePlan router_plan(int T, int H, int E, int x_is_bf16) {
+  RoutePlan p{};
+  p.eb = (E + 15) / 16;
+  if (!x_is_bf16) {
+    p.ksn = 1;
+    return p;
+  }
+  // 64-token tiles, one expert block per wave: few registers, many waves
+  p.mbt = 4;
+  p.ebw = 1;
+  const int tiles = ((T + 16 * p.mbt - 1) / (16 * p.mbt)) * ((p.eb + 4 * p.ebw - 1) / (4 * p.ebw));
+  const int nst = H / 64;
+  // about a thousand workgroups, but at most 16 slices for the top-k pass to add
+  int ksn = 1;
+  while (tiles * ksn < 1024 && ksn < 16 && ksn * 2 <= nst && nst % (ksn * 2) == 0) ksn *= 2;
+  p.ksn = ksn;
+  p.nsl = nst / ksn;
+  return p;
 }
 
 size_t route_ws_bytes(int T, int H, int E, int x_is_bf16) {
-  int ksn, kl;
-  router_plan(T, H, x_is_bf16, ksn, kl);
-  return (size_t)ksn * T * E * sizeof(float);
+  const RoutePlan p = router_plan(T, H, E, x_is_bf16);
+  size_t bytes = (size_t)p.ksn * T * E * sizeof(float);
+  if (x_is_bf16) {
+    bytes = (bytes + 255) & ~(size_t)255;
+    bytes += (size_t)3 * p.eb * H * 32;   // split weights: 3 terms x 16 rows x 2 bytes per element
+  }
+  return bytes;
 }
 
 hipError_t launch_route(const void *x, int x_is_bf16, const float *Wr, const float *bias,
@@ -255,16 +404,19 @@ hipError_t launch_route(const void *x, int x_is_bf16, const float *Wr, const flo
                         float rho, int route_norm, hipStream_t stream) {
   if (T <= 0) return hipSuccess;
   dim3 blk(256);
-  int ksn, kl;
-  router_plan(T, H, x_is_bf16, ksn, kl);
+  const RoutePlan p = router_plan(T, H, E, x_is_bf16);
+  const int ksn = p.ksn;
   if (x_is_bf16) {
-    if (T <= 256) {
-      dim3 grid((T + 15) / 16, (E + 63) / 64, ksn);
-      router_mfma_kernel<1><<<grid, blk, 0, stream>>>((const uint16_t *)x, Wr, part, T, H, E, kl);
-    } else {
-      dim3 grid((T + 63) / 64, (E + 63) / 64, ksn);
-      router_mfma_kernel<4><<<grid, blk, 0, stream>>>((const uint16_t *)x, Wr, part, T, H, E, kl);
-    }
+    const size_t pbytes = (((size_t)ksn * T * E * sizeof(float)) + 255) & ~(size_t)255;
+    uint4 *wsplit = (uint4 *)((char *)part + pbytes);
+    const long long nthr = (long long)p.eb * (H / 64) * 128;
+    router_split_kernel<<<(unsigned)((nthr + 255) / 256), blk, 0, stream>>>(Wr, E, H, p.eb, wsplit);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int n_et = (p.eb + 3) / 4, n_tt = (T + 16 * p.mbt - 1) / (16 * p.mbt);
+    const int per_xcd = (n_et * n_tt * ksn + 7) / 8;
+    router_gemm_kernel<4, 2><<<per_xcd * 8, blk, 0, stream>>>((const uint16_t *)x, wsplit, part, T,
+                                                               H, E, p.eb, p.nsl, n_et, n_tt, ksn);
   } else {
     if (T <= 256) {
       dim3 grid((T + 15) / 16, (E + 63) / 64);
