@@ -496,20 +496,22 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
     xa = b + L.xq;
     xs = (const uint8_t *)b + L.xs;
   }
-  // Shared expert: it needs only the activations, so the side stream starts
-  // it at once and it runs beside gating, permutation and the routed GEMMs.
+  // Shared expert on the side stream.  It needs only the activations, so it
+  // starts at once and runs beside gating, permutation and the routed GEMMs.
   const bool two = has_shared && ctx->side && ctx->side != s;
-  if (has_shared) {
+  auto shared_expert = [&]() -> hipError_t {
     hipStream_t ss = two ? ctx->side : s;
+    hipError_t e;
     if (two) {
-      MOE_TRY(hipEventRecord(ctx->ev_ready, s), "input-ready event");
-      MOE_TRY(hipStreamWaitEvent(ss, ctx->ev_ready, 0), "side stream wait");
+      if ((e = hipEventRecord(ctx->ev_ready, s)) != hipSuccess) return e;
+      if ((e = hipStreamWaitEvent(ss, ctx->ev_ready, 0)) != hipSuccess) return e;
     }
-    MOE_TRY(ffn(desc, w, 1, xa, xs, T, nullptr, nullptr, b + L.z, b + L.sh_h,
-                mx ? (uint8_t *)b + L.sh_hs : nullptr, ss, &tm),
-            "shared expert");
-    if (two) MOE_TRY(hipEventRecord(ctx->ev_done, ss), "shared-done event");
-  }
+    e = ffn(desc, w, 1, xa, xs, T, nullptr, nullptr, b + L.z, b + L.sh_h,
+            mx ? (uint8_t *)b + L.sh_hs : nullptr, ss, &tm);
+    if (e != hipSuccess) return e;
+    return two ? hipEventRecord(ctx->ev_done, ss) : hipSuccess;
+  };
+  if (has_shared) MOE_TRY(shared_expert(), "shared expert");
   // Gating on the main stream.
   MOE_TRY(tm.start(MOE_STAGE_ROUTE, s), "timing");
   MOE_TRY(launch_route(x, desc->act_dtype == MOE_BF16, w->router_w, w->router_bias,

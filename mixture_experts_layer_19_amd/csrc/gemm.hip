@@ -25,6 +25,13 @@
 #ifndef MOE_TILE_MAP
 #define MOE_TILE_MAP 0
 #endif
+// streaming kernel at decode sizes: weight blocks per wave, explicit prefetch
+#ifndef MOE_SKINNY_NW
+#define MOE_SKINNY_NW 4
+#endif
+#ifndef MOE_SKINNY_PF
+#define MOE_SKINNY_PF 0
+#endif
 // m-tiles per group in the tiled kernel's tile order
 #ifndef MOE_TILE_GM
 #define MOE_TILE_GM 8
@@ -45,14 +52,6 @@
 #endif
 #ifndef MOE_TILE_OCC
 #define MOE_TILE_OCC 2
-#endif
-// cache-policy bits of the weight loads
-#ifndef MOE_TILE_WAUX
-#define MOE_TILE_WAUX 0
-#endif
-// pin the interleaving of LDS reads and products with scheduling groups
-#ifndef MOE_TILE_SGB
-#define MOE_TILE_SGB 0
 #endif
 // workgroups per CU the MX-fp8 tiled kernel is compiled for
 #ifndef MOE_TILE_OCC_MX
@@ -525,8 +524,8 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     for (int n = 0; n < NBW; ++n) {
       const uint32_t so = (uint32_t)(n * kcn + kc) * kBlockBytes + h * 2048;
       wr[set][n] = make_frag<F>(
-          __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)so, MOE_TILE_WAUX),
-          __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)(so + 1024), MOE_TILE_WAUX));
+          __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)so, 0),
+          __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)(so + 1024), 0));
       wsr[set][n] = 0;
       if constexpr (F == FMT_MX8)
         wsr[set][n] = (__builtin_amdgcn_raw_buffer_load_b16(wsrs, (int)wsvoff,
@@ -570,24 +569,20 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
       tsf[b] = 0;
       if constexpr (F == FMT_MX8) tsf[b] = tscl[slot][(wm * MBW + m) * 64 + lane];
     };
+    // bf16: pin the order (the two LDS reads of block m + 1, then the eight
+    // products of block m) with scheduling groups
     read_frag(0, 0);
-#if MOE_TILE_SGB
     if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#endif
 #pragma unroll
     for (int m = 0; m < MBW; ++m) {
       if (m + 1 < MBW) {
         read_frag(m + 1, (m + 1) & 1);
-#if MOE_TILE_SGB
         if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
-#endif
       }
 #pragma unroll
       for (int n = 0; n < NBW; ++n)
         mfma_frag<F>(acc[n][m], wr[set][n], tf[m & 1], wsr[set][n], tsf[m & 1]);
-#if MOE_TILE_SGB
       if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NBW, 0);
-#endif
     }
     __builtin_amdgcn_sched_barrier(0);
     store_tokens(s + 1);
@@ -674,7 +669,7 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     if (per <= 64) return launch_skinny<F, EPI, OT, NWS, 4, 4>(g, 1, stream);
   } else if (g.rows <= 64 * g.k_route) {
     // at most T <= 64 rows per expert: the streaming kernel takes them all
-    if (per <= 16) return launch_skinny<F, EPI, OT, 4, 1, 1>(g, segs, stream);
+    if (per <= 16) return launch_skinny<F, EPI, OT, MOE_SKINNY_NW, 1, 1, MOE_SKINNY_PF>(g, segs, stream);
     if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
     return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
   } else {
