@@ -32,6 +32,17 @@
 #ifndef MOE_SKINNY_PF
 #define MOE_SKINNY_PF 0
 #endif
+// streaming kernel for the short segments of a mixed launch: weight blocks
+// per wave, token blocks per pass
+#ifndef MOE_HYB_NW
+#define MOE_HYB_NW 4
+#endif
+#ifndef MOE_HYB_MB
+#define MOE_HYB_MB 2
+#endif
+#ifndef MOE_HYB_SPLIT
+#define MOE_HYB_SPLIT 32
+#endif
 // m-tiles per group in the tiled kernel's tile order
 #ifndef MOE_TILE_GM
 #define MOE_TILE_GM 8
@@ -59,7 +70,7 @@
 #endif
 // token rows per tile of the MX-fp8 tiled kernel
 #ifndef MOE_TILE_TM_MX
-#define MOE_TILE_TM_MX 64
+#define MOE_TILE_TM_MX 128
 #endif
 
 namespace moe {
@@ -673,11 +684,12 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
     return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
   } else {
-    // experts of at most 64 rows go to the streaming kernel, the longer
-    // ones to the tiled kernel (the split is applied on the device, where
-    // the counts are)
-    g.split = 64;
-    hipError_t err = launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
+    // experts of at most MOE_HYB_SPLIT rows go to the streaming kernel, the
+    // longer ones to the tiled kernel (the split is applied on the device,
+    // where the counts are)
+    g.split = MOE_HYB_SPLIT;
+    constexpr int HNW = (EPI == EPI_SWIGLU && OT == FMT_MX8) ? 4 : MOE_HYB_NW;
+    hipError_t err = launch_skinny<F, EPI, OT, HNW, MOE_HYB_MB, 1>(g, segs, stream);
     if (err != hipSuccess) return err;
   }
   if constexpr (F == FMT_MX8) {
