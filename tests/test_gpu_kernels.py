@@ -127,6 +127,26 @@ def test_route_parity(orc, ctx, name, T):
     assert np.abs(g_w.astype(np.float64).sum(1) - 2.826).max() <= 1e-5
 
 
+@pytest.mark.parametrize("E,H,T,k,beta", [(40, 512, 77, 6, 0.0), (24, 256, 1, 3, 0.0),
+                                          (200, 768, 300, 8, 0.38), (16, 2048, 129, 4, 0.0)])
+def test_route_parity_bf16_shapes(orc, ctx, E, H, T, k, beta):
+    """bf16 routing at expert counts that leave a partial 16-expert block or
+    a partial 64-expert tile, ragged token counts, and K split into slices
+    of different lengths (H / 64 stages)."""
+    w = I.workload("hy3_decode", T=T, H=H, E=E, k=k, zipf_beta=beta)
+    xg, x = I.x_input(w)
+    Wr, b = I.router_weight(w), I.router_bias(w)
+    g_idx, g_w = _route_gpu(ctx, w, dev(xg), T, dev(Wr), None if b is None else dev(b))
+    o_idx, o_w, scores, gap = orc.route(x, Wr, b, w.k, w.rho, w.route_norm)
+    mism, flips = classify_routing(g_idx, o_idx, scores)
+    print("[route bf16] E=%d H=%d T=%d: %d mismatching, %d tie flips" % (E, H, T, mism.sum(),
+                                                                      flips.sum()))
+    assert not (mism & ~flips).any(), np.nonzero(mism & ~flips)[0][:10]
+    ok = ~mism
+    rel = np.abs(g_w[ok].astype(np.float64) - o_w[ok]) / np.abs(o_w[ok])
+    assert rel.max() <= 1e-6, rel.max()
+
+
 def test_route_zero_router_ties_to_lowest_indices(ctx):
     w = I.workload("tiny")
     xg, _ = I.x_input(w)
