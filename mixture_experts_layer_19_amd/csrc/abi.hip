@@ -21,7 +21,7 @@
 struct moe_ctx {
   int device;
   hipStream_t side;
-  hipEvent_t ev_ready;   // recorded on the caller's stream after gating
+  hipEvent_t ev_ready;   // recorded on the caller's stream once the routed gate/up is queued
   hipEvent_t ev_done;    // recorded on the side stream after the shared expert
   char last_error[256];
   int profiling;
@@ -138,7 +138,8 @@ moe_status check_ctx(moe_ctx *ctx) {
 // format (xa: x itself for f32/bf16, the MX codes for MX-fp8).
 hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *xa,
                const uint8_t *xs, int T, const int32_t *sorted_src, const int32_t *offsets,
-               void *y, void *h, uint8_t *hs, hipStream_t s, StageTimer *tm = nullptr) {
+               void *y, void *h, uint8_t *hs, hipStream_t s, StageTimer *tm = nullptr,
+               hipEvent_t after_first = nullptr) {
   const int st1 = shared ? MOE_STAGE_SHARED_GATE_UP : MOE_STAGE_GATE_UP;
   const int st2 = shared ? MOE_STAGE_SHARED_DOWN : MOE_STAGE_DOWN;
   const int F = fmt_of(d->expert_dtype);
@@ -173,6 +174,7 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   err = launch_grouped_gemm(g1, F, EPI_SWIGLU, F, rows, s);
   if (err != hipSuccess) return err;
   if (tm && (err = tm->stop(st1, s)) != hipSuccess) return err;
+  if (after_first && (err = hipEventRecord(after_first, s)) != hipSuccess) return err;
 
   GemmArgs g2;
   memset(&g2, 0, sizeof g2);
@@ -496,22 +498,21 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
     xa = b + L.xq;
     xs = (const uint8_t *)b + L.xs;
   }
-  // Shared expert on the side stream.  It needs only the activations, so it
-  // starts at once and runs beside gating, permutation and the routed GEMMs.
+  // Shared expert on the side stream.  It needs only the activations; it is
+  // started once the routed gate/up GEMM is queued (the input-ready event is
+  // recorded after it), so it runs beside the routed down GEMM: beside gating
+  // and permutation it slows those short, latency-bound kernels by more than
+  // it saves.
   const bool two = has_shared && ctx->side && ctx->side != s;
   auto shared_expert = [&]() -> hipError_t {
     hipStream_t ss = two ? ctx->side : s;
     hipError_t e;
-    if (two) {
-      if ((e = hipEventRecord(ctx->ev_ready, s)) != hipSuccess) return e;
-      if ((e = hipStreamWaitEvent(ss, ctx->ev_ready, 0)) != hipSuccess) return e;
-    }
+    if (two && (e = hipStreamWaitEvent(ss, ctx->ev_ready, 0)) != hipSuccess) return e;
     e = ffn(desc, w, 1, xa, xs, T, nullptr, nullptr, b + L.z, b + L.sh_h,
             mx ? (uint8_t *)b + L.sh_hs : nullptr, ss, &tm);
     if (e != hipSuccess) return e;
     return two ? hipEventRecord(ctx->ev_done, ss) : hipSuccess;
   };
-  if (has_shared) MOE_TRY(shared_expert(), "shared expert");
   // Gating on the main stream.
   MOE_TRY(tm.start(MOE_STAGE_ROUTE, s), "timing");
   MOE_TRY(launch_route(x, desc->act_dtype == MOE_BF16, w->router_w, w->router_bias,
@@ -526,8 +527,9 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
           "permutation");
   MOE_TRY(tm.stop(MOE_STAGE_PERMUTE, s), "timing");
   MOE_TRY(ffn(desc, w, 0, xa, xs, T, src, offsets, b + L.y, b + L.h,
-              mx ? (uint8_t *)b + L.hs : nullptr, s, &tm),
+              mx ? (uint8_t *)b + L.hs : nullptr, s, &tm, two ? ctx->ev_ready : nullptr),
           "routed experts");
+  if (has_shared) MOE_TRY(shared_expert(), "shared expert");
   // Join, then FinalizeRouting + shared add.
   if (two) MOE_TRY(hipStreamWaitEvent(s, ctx->ev_done, 0), "main stream wait");
   const int of = fmt_of(desc->out_dtype);
