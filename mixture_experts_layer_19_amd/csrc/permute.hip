@@ -101,6 +101,59 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
   }
 }
 
+// All three phases in one workgroup, for a single token block (T <= 256):
+// the bitmap columns stay in LDS, and one launch replaces three.
+__global__ __launch_bounds__(256) void perm_single_kernel(
+    const int32_t *__restrict__ topk_idx, int T, int E, int k, int32_t *__restrict__ counts,
+    int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_src, int32_t *__restrict__ dest) {
+  extern __shared__ uint32_t col[];           // [E][kPermWords], then tot[1024]
+  int32_t *tot = (int32_t *)(col + E * kPermWords);
+  const int tid = threadIdx.x;
+  for (int i = tid; i < E * kPermWords; i += 256) col[i] = 0u;
+  for (int e = tid; e < 1024; e += 256) tot[e] = 0;
+  __syncthreads();
+  if (tid < T) {
+    for (int j = 0; j < k; ++j) {
+      int e = topk_idx[(size_t)tid * k + j];
+      if (e >= 0 && e < E) atomicOr(&col[e * kPermWords + (tid >> 5)], 1u << (tid & 31));
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
+    int c = 0;
+#pragma unroll
+    for (int w = 0; w < kPermWords; ++w) c += __popc(col[e * kPermWords + w]);
+    counts[e] = c;
+    tot[e] = c;
+  }
+  __syncthreads();
+  // Hillis-Steele inclusive scan over 1024 entries (E <= 1024).
+  for (int d = 1; d < 1024; d <<= 1) {
+    int v[4];
+    int n = 0;
+    for (int e = tid; e < 1024; e += 256) v[n++] = (e >= d) ? tot[e - d] : 0;
+    __syncthreads();
+    n = 0;
+    for (int e = tid; e < 1024; e += 256) tot[e] += v[n++];
+    __syncthreads();
+  }
+  for (int e = tid; e <= E; e += 256) offsets[e] = (e == 0) ? 0 : tot[e - 1];
+  if (tid >= T) return;
+  const int word = tid >> 5;
+  const uint32_t below = (1u << (tid & 31)) - 1u;
+  for (int j = 0; j < k; ++j) {
+    const int f = tid * k + j;
+    const int e = topk_idx[f];
+    if (e < 0 || e >= E) continue;
+    const uint32_t *c = col + e * kPermWords;
+    int rank = __popc(c[word] & below);
+    for (int w = 0; w < word; ++w) rank += __popc(c[w]);
+    const int r = (e == 0 ? 0 : tot[e - 1]) + rank;
+    sorted_src[r] = f;
+    dest[f] = r;
+  }
+}
+
 size_t permute_ws_bytes(int T, int E) {
   size_t nblk = (size_t)(T + kPermBlock - 1) / kPermBlock;
   size_t b = nblk * E * kPermWords * sizeof(uint32_t);
@@ -121,6 +174,12 @@ hipError_t launch_permute(const int32_t *topk_idx, int T, int E, int k, int32_t 
   uint32_t *bits = (uint32_t *)ws;
   int32_t *blk_count = (int32_t *)((char *)ws + nb);
   int32_t *blk_base = (int32_t *)((char *)ws + nb + nc);
+  if (nblk == 1) {
+    const size_t lds = (size_t)E * kPermWords * sizeof(uint32_t) + 1024 * sizeof(int32_t);
+    perm_single_kernel<<<1, 256, lds, stream>>>(topk_idx, T, E, k, counts, offsets, sorted_src,
+                                                dest);
+    return hipGetLastError();
+  }
   if (nblk > 0) {
     perm_count_kernel<<<nblk, 256, (size_t)E * kPermWords * sizeof(uint32_t), stream>>>(
         topk_idx, T, E, k, bits, blk_count);
