@@ -25,6 +25,14 @@
 #ifndef MOE_TILE_MAP
 #define MOE_TILE_MAP 0
 #endif
+// Dynamic LDS reserved per workgroup of the decode streaming kernel, which
+// uses none: it caps residency at 3 workgroups per CU.  Fewer concurrent
+// weight streams read HBM faster here (6.35 -> 6.5 TB/s), and the shared
+// expert's workgroups on the side stream find free slots instead of waiting
+// for the routed GEMM to drain.
+#ifndef MOE_SKINNY_LDS_PAD
+#define MOE_SKINNY_LDS_PAD 45000
+#endif
 // streaming kernel at decode sizes: weight blocks per wave, explicit prefetch
 #ifndef MOE_SKINNY_NW
 #define MOE_SKINNY_NW 4
@@ -636,7 +644,8 @@ static hipError_t launch_skinny(const GemmArgs &g, int segs, hipStream_t stream)
   constexpr int BPW = (KSW == 4) ? NW : 4 * NW;
   const int nbtot = g.N / 16;
   if (nbtot % BPW) return hipErrorInvalidValue;
-  gemm_skinny_kernel<F, EPI, OT, NW, MB, KSW, PF><<<segs * (nbtot / BPW), 256, 0, stream>>>(g);
+  gemm_skinny_kernel<F, EPI, OT, NW, MB, KSW, PF>
+      <<<segs * (nbtot / BPW), 256, (KSW == 1 && MB == 1) ? MOE_SKINNY_LDS_PAD : 0, stream>>>(g);
   return hipGetLastError();
 }
 
