@@ -76,9 +76,11 @@
 #ifndef MOE_TILE_OCC_MX
 #define MOE_TILE_OCC_MX 2
 #endif
-// token rows per tile of the MX-fp8 tiled kernel
+// token rows per tile of the MX-fp8 tiled kernel: 96 covers the ~171 rows
+// an expert gets at 4096 tokens (top-8 of 192) in two m-tiles with 11%
+// padding, where 128 pads by 33%
 #ifndef MOE_TILE_TM_MX
-#define MOE_TILE_TM_MX 128
+#define MOE_TILE_TM_MX 96
 #endif
 
 namespace moe {
@@ -256,10 +258,11 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < MB; ++i) {
           if (i >= live) continue;
-          mfma_half<F>(acc[n][i], bf.w[n][0], bf.w[n][1], bf.t[i][0], bf.t[i][1], bf.ws[n] & 0xFF,
-                       bf.ts[i] & 0xFF);
-          mfma_half<F>(acc[n][i], bf.w[n][2], bf.w[n][3], bf.t[i][2], bf.t[i][3], bf.ws[n] >> 8,
-                       bf.ts[i] >> 8);
+          // MX: byte h of the scale pairs is half h's scale
+          mfma_half<F, 0, 0>(acc[n][i], bf.w[n][0], bf.w[n][1], bf.t[i][0], bf.t[i][1], bf.ws[n],
+                             bf.ts[i]);
+          mfma_half<F, 1, 1>(acc[n][i], bf.w[n][2], bf.w[n][3], bf.t[i][2], bf.t[i][3], bf.ws[n],
+                             bf.ts[i]);
         }
     };
 
@@ -526,10 +529,10 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     if constexpr (F == FMT_MX8) {
 #pragma unroll
       for (int i = 0; i < TSL; ++i)
-        // (a runtime test only for a partial last round: a branch here would
-        // split the stage into several blocks for the scheduler)
-        if ((i + 1) * NTH <= MBT * 64 || tid + NTH * i < MBT * 64)
-          tscl[s & 1][tid + NTH * i] = (uint8_t)tsreg[i];
+        // in a partial last round the surplus threads write the last entry
+        // again, with the value its owner writes (they loaded it from the
+        // same clamped offset): no branch, so the stage stays one block
+        tscl[s & 1][min(tid + NTH * i, MBT * 64 - 1)] = (uint8_t)tsreg[i];
     }
   };
   // NSET = WPF + 1 register sets of weight fragments: stage s multiplies
@@ -545,11 +548,12 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
       wr[set][n] = make_frag<F>(
           __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)so, 0),
           __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)(so + 1024), 0));
+      // MX: the raw scale pair of this chunk (byte h is this half's; the
+      // product selects it), so nothing waits on the load before its use
       wsr[set][n] = 0;
       if constexpr (F == FMT_MX8)
-        wsr[set][n] = (__builtin_amdgcn_raw_buffer_load_b16(wsrs, (int)wsvoff,
-                                                            (n * kcn + kc) * 128, 0) >>
-                       (8 * h)) & 0xFFu;
+        wsr[set][n] = __builtin_amdgcn_raw_buffer_load_b16(wsrs, (int)wsvoff,
+                                                           (n * kcn + kc) * 128, 0);
     }
   };
 
@@ -600,7 +604,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
       }
 #pragma unroll
       for (int n = 0; n < NBW; ++n)
-        mfma_frag<F>(acc[n][m], wr[set][n], tf[m & 1], wsr[set][n], tsf[m & 1]);
+        mfma_frag<F, slot>(acc[n][m], wr[set][n], tf[m & 1], wsr[set][n], tsf[m & 1]);
       if constexpr (F == FMT_BF16) __builtin_amdgcn_sched_group_barrier(0x008, 2 * NBW, 0);
     }
     __builtin_amdgcn_sched_barrier(0);

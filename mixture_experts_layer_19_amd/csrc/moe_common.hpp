@@ -142,8 +142,10 @@ __device__ __forceinline__ int tslot(int r16, int g, int p) {
 
 // acc += W x T over one half-chunk.  w0, w1 / t0, t1: the lane's two
 // 16-byte pieces of this half (pieces 2h and 2h + 1).  ws, ts: E8M0 scale
-// bytes of the lane's MX block in bits 7:0 (MX only; opsel 0 selects them).
-template <int F>
+// bytes of the lane's MX block (MX only): the weight scale is byte WSEL of
+// ws and the token scale byte TSEL of ts (the instruction's operand selects
+// pick them, so a packed pair of scales needs no shift).
+template <int F, int WSEL = 0, int TSEL = 0>
 __device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32x4 &w1,
                                           const i32x4 &t0, const i32x4 &t1, uint32_t ws,
                                           uint32_t ts) {
@@ -164,8 +166,9 @@ __device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32
   } else {
     const i32x8 a = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
     const i32x8 b = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
-    // operand format 0 = fp8 E4M3 for A and B; opsel 0 = scale byte 0
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, (int)ws, 0, (int)ts);
+    // operand format 0 = fp8 E4M3 for A and B; scale bytes WSEL and TSEL
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, WSEL, (int)ws, TSEL,
+                                                           (int)ts);
   }
 }
 
@@ -193,11 +196,11 @@ __device__ __forceinline__ Frag<F> make_frag(const i32x4 &a, const i32x4 &b) {
   return f;
 }
 
-template <int F>
+template <int F, int WSEL = 0>
 __device__ __forceinline__ void mfma_frag(f32x4 &acc, const Frag<F> &w, const Frag<F> &t,
                                           uint32_t ws, uint32_t ts) {
   if constexpr (F == FMT_MX8) {
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.v, t.v, acc, 0, 0, 0, (int)ws, 0,
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.v, t.v, acc, 0, 0, WSEL, (int)ws, 0,
                                                            (int)ts);
   } else {
     mfma_half<F>(acc, w.p0, w.p1, t.p0, t.p1, ws, ts);

@@ -308,6 +308,20 @@ def test_shared_ffn_parity(orc, ctx, dtype, T):
     assert err <= TOL[dtype], err
 
 
+@pytest.mark.parametrize("dtype,H,I_,E,k,T", [
+    # more tiles than one round of resident workgroups, ragged expert
+    # segments, and a down GEMM of a single K chunk (two stages)
+    ("bf16", 256, 128, 16, 8, 16384),
+    ("bf16", 512, 256, 10, 8, 6000),
+    ("f32", 256, 128, 16, 8, 8192),
+])
+def test_grouped_ffn_many_tiles(orc, ctx, dtype, H, I_, E, k, T):
+    w = I.Workload("many", T=T, H=H, E=E, k=k, I=I_, Is=I_, dtype=dtype)
+    err = _ffn_case(orc, ctx, w, T, tag=3)
+    print("[ffn many tiles] %s T=%d rel err %.3g" % (dtype, T, err))
+    assert err <= TOL[dtype], err
+
+
 def test_grouped_ffn_uneven_segments(orc, ctx):
     # one expert takes most rows, two are empty: tiled kernel with many
     # m-tiles in one segment and skipped experts
