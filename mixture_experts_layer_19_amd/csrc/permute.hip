@@ -56,8 +56,20 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restric
   for (int e = tid; e < 1024; e += blockDim.x) tot[e] = 0;
   __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
-    int run = 0;
-    for (int b = 0; b < nblk; ++b) {
+    // eight block counts are read before any is added, so eight loads are
+    // in flight instead of one
+    int run = 0, b = 0;
+    for (; b + 8 <= nblk; b += 8) {
+      int c[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) c[u] = blk_count[(size_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        blk_base[(size_t)(b + u) * E + e] = run;
+        run += c[u];
+      }
+    }
+    for (; b < nblk; ++b) {
       blk_base[(size_t)b * E + e] = run;
       run += blk_count[(size_t)b * E + e];
     }
@@ -78,12 +90,20 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restric
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = (e == 0) ? 0 : tot[e - 1];
 }
 
-// Phase 3: every pair computes its row and writes both directions.
+// Phase 3: every pair computes its row and writes both directions.  The
+// block's bitmap columns and its first row per expert are staged in LDS
+// first (coalesced), so the ranks read no global memory.
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const int32_t *__restrict__ topk_idx, int T, int E, int k, const uint32_t *__restrict__ bits,
     const int32_t *__restrict__ blk_base, const int32_t *__restrict__ offsets,
     int32_t *__restrict__ sorted_src, int32_t *__restrict__ dest) {
+  extern __shared__ uint32_t col[];           // [E][kPermWords], then first row [E]
+  int32_t *first = (int32_t *)(col + E * kPermWords);
   const int b = blockIdx.x, tid = threadIdx.x;
+  const uint32_t *bb = bits + (size_t)b * E * kPermWords;
+  for (int i = tid; i < E * kPermWords; i += 256) col[i] = bb[i];
+  for (int e = tid; e < E; e += 256) first[e] = offsets[e] + blk_base[(size_t)b * E + e];
+  __syncthreads();
   const int t = b * kPermBlock + tid;
   if (t >= T) return;
   const int word = tid >> 5;
@@ -92,10 +112,10 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const int f = t * k + j;
     const int e = topk_idx[f];
     if (e < 0 || e >= E) continue;
-    const uint32_t *c = bits + ((size_t)b * E + e) * kPermWords;
+    const uint32_t *c = col + e * kPermWords;
     int rank = __popc(c[word] & below);
     for (int w = 0; w < word; ++w) rank += __popc(c[w]);
-    const int r = offsets[e] + blk_base[(size_t)b * E + e] + rank;
+    const int r = first[e] + rank;
     sorted_src[r] = f;
     dest[f] = r;
   }
@@ -189,8 +209,8 @@ hipError_t launch_permute(const int32_t *topk_idx, int T, int E, int k, int32_t 
   perm_scan_kernel<<<1, 256, 0, stream>>>(blk_count, nblk, E, blk_base, counts, offsets);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
-  perm_scatter_kernel<<<nblk, 256, 0, stream>>>(topk_idx, T, E, k, bits, blk_base, offsets,
-                                                sorted_src, dest);
+  perm_scatter_kernel<<<nblk, 256, (size_t)E * (kPermWords + 1) * sizeof(uint32_t), stream>>>(
+      topk_idx, T, E, k, bits, blk_base, offsets, sorted_src, dest);
   return hipGetLastError();
 }
 

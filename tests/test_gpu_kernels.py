@@ -207,7 +207,19 @@ def test_permute_skewed_counts(orc, ctx):
 @pytest.mark.parametrize("name,T,shared", [("tiny", 64, True), ("tiny", 13, False),
                                            ("hy3_decode", 64, True), ("hy3_decode", 300, False)])
 def test_combine_parity(orc, ctx, name, T, shared):
-    w = I.workload(name, T=T)
+    _combine_case(orc, ctx, I.workload(name, T=T), T, shared)
+
+
+@pytest.mark.parametrize("dtype,k,H,shared", [("bf16", 6, 2560, True), ("f32", 6, 2560, False),
+                                              ("bf16", 3, 768, False)])
+def test_combine_other_k_and_widths(orc, ctx, dtype, k, H, shared):
+    # k other than 4 and 8 (read at run time), rows of more than one
+    # 2048-column slice with a partial last slice, and a row narrower than one
+    w = I.Workload("comb", T=37, H=H, E=10, k=k, I=128, Is=128, dtype=dtype)
+    _combine_case(orc, ctx, w, 37, shared)
+
+
+def _combine_case(orc, ctx, w, T, shared):
     d = desc_for(w)
     rng = I.aux_stream(w, 7)
     idx = I.random_topk(w, T, tag=3)
