@@ -17,19 +17,50 @@ namespace moe {
 constexpr int kPermBlock = 256;               // tokens per block
 constexpr int kPermWords = kPermBlock / 32;   // bitmap words per (block, expert)
 
+constexpr int kMaxChoices = 16;               // largest k the library accepts
+
+// The k expert indices of token t, all read before any is used so that the
+// loads are in flight together: KT = 4 or 8 reads 16-byte vectors (the
+// caller checks the alignment), KT = 0 reads k scalars (entries past k
+// repeat the last one and are not used).
+template <int KT>
+__device__ __forceinline__ void load_choices(const int32_t *__restrict__ topk_idx, int t, int k,
+                                             int (&ev)[kMaxChoices]) {
+  if constexpr (KT == 4 || KT == 8) {
+    const int4 *p = (const int4 *)(topk_idx + (size_t)t * KT);
+#pragma unroll
+    for (int q = 0; q < KT / 4; ++q) {
+      const int4 v = p[q];
+      ev[4 * q] = v.x;
+      ev[4 * q + 1] = v.y;
+      ev[4 * q + 2] = v.z;
+      ev[4 * q + 3] = v.w;
+    }
+  } else {
+#pragma unroll
+    for (int j = 0; j < kMaxChoices; ++j) ev[j] = topk_idx[(size_t)t * k + min(j, k - 1)];
+  }
+}
+
 // Phase 1: per token block, the bitmap column of every expert and its count.
+template <int KT>
 __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t *__restrict__ topk_idx, int T,
                                                          int E, int k, uint32_t *__restrict__ bits,
                                                          int32_t *__restrict__ blk_count) {
+  constexpr int KM = KT > 0 ? KT : kMaxChoices;
   extern __shared__ uint32_t col[];           // [E][kPermWords]
   const int b = blockIdx.x, tid = threadIdx.x;
   for (int i = tid; i < E * kPermWords; i += 256) col[i] = 0u;
-  __syncthreads();
   const int t = b * kPermBlock + tid;
+  int ev[kMaxChoices];
+  if (t < T) load_choices<KT>(topk_idx, t, k, ev);
+  __syncthreads();
   if (t < T) {
-    for (int j = 0; j < k; ++j) {
-      int e = topk_idx[(size_t)t * k + j];
-      if (e >= 0 && e < E) atomicOr(&col[e * kPermWords + (tid >> 5)], 1u << (tid & 31));
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int e = ev[j];
+      if ((KT > 0 || j < k) && e >= 0 && e < E)
+        atomicOr(&col[e * kPermWords + (tid >> 5)], 1u << (tid & 31));
     }
   }
   __syncthreads();
@@ -93,25 +124,30 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restric
 // Phase 3: every pair computes its row and writes both directions.  The
 // block's bitmap columns and its first row per expert are staged in LDS
 // first (coalesced), so the ranks read no global memory.
+template <int KT>
 __global__ __launch_bounds__(256) void perm_scatter_kernel(
     const int32_t *__restrict__ topk_idx, int T, int E, int k, const uint32_t *__restrict__ bits,
     const int32_t *__restrict__ blk_base, const int32_t *__restrict__ offsets,
     int32_t *__restrict__ sorted_src, int32_t *__restrict__ dest) {
+  constexpr int KM = KT > 0 ? KT : kMaxChoices;
   extern __shared__ uint32_t col[];           // [E][kPermWords], then first row [E]
   int32_t *first = (int32_t *)(col + E * kPermWords);
   const int b = blockIdx.x, tid = threadIdx.x;
+  const int t = b * kPermBlock + tid;
+  int ev[kMaxChoices];
+  if (t < T) load_choices<KT>(topk_idx, t, k, ev);
   const uint32_t *bb = bits + (size_t)b * E * kPermWords;
   for (int i = tid; i < E * kPermWords; i += 256) col[i] = bb[i];
   for (int e = tid; e < E; e += 256) first[e] = offsets[e] + blk_base[(size_t)b * E + e];
   __syncthreads();
-  const int t = b * kPermBlock + tid;
   if (t >= T) return;
   const int word = tid >> 5;
   const uint32_t below = (1u << (tid & 31)) - 1u;
-  for (int j = 0; j < k; ++j) {
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
     const int f = t * k + j;
-    const int e = topk_idx[f];
-    if (e < 0 || e >= E) continue;
+    const int e = ev[j];
+    if ((KT == 0 && j >= k) || e < 0 || e >= E) continue;
     const uint32_t *c = col + e * kPermWords;
     int rank = __popc(c[word] & below);
     for (int w = 0; w < word; ++w) rank += __popc(c[w]);
@@ -123,19 +159,25 @@ __global__ __launch_bounds__(256) void perm_scatter_kernel(
 
 // All three phases in one workgroup, for a single token block (T <= 256):
 // the bitmap columns stay in LDS, and one launch replaces three.
+template <int KT>
 __global__ __launch_bounds__(256) void perm_single_kernel(
     const int32_t *__restrict__ topk_idx, int T, int E, int k, int32_t *__restrict__ counts,
     int32_t *__restrict__ offsets, int32_t *__restrict__ sorted_src, int32_t *__restrict__ dest) {
+  constexpr int KM = KT > 0 ? KT : kMaxChoices;
   extern __shared__ uint32_t col[];           // [E][kPermWords], then tot[1024]
   int32_t *tot = (int32_t *)(col + E * kPermWords);
   const int tid = threadIdx.x;
+  int ev[kMaxChoices];
+  if (tid < T) load_choices<KT>(topk_idx, tid, k, ev);
   for (int i = tid; i < E * kPermWords; i += 256) col[i] = 0u;
   for (int e = tid; e < 1024; e += 256) tot[e] = 0;
   __syncthreads();
   if (tid < T) {
-    for (int j = 0; j < k; ++j) {
-      int e = topk_idx[(size_t)tid * k + j];
-      if (e >= 0 && e < E) atomicOr(&col[e * kPermWords + (tid >> 5)], 1u << (tid & 31));
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
+      const int e = ev[j];
+      if ((KT > 0 || j < k) && e >= 0 && e < E)
+        atomicOr(&col[e * kPermWords + (tid >> 5)], 1u << (tid & 31));
     }
   }
   __syncthreads();
@@ -161,10 +203,11 @@ __global__ __launch_bounds__(256) void perm_single_kernel(
   if (tid >= T) return;
   const int word = tid >> 5;
   const uint32_t below = (1u << (tid & 31)) - 1u;
-  for (int j = 0; j < k; ++j) {
+#pragma unroll
+  for (int j = 0; j < KM; ++j) {
     const int f = tid * k + j;
-    const int e = topk_idx[f];
-    if (e < 0 || e >= E) continue;
+    const int e = ev[j];
+    if ((KT == 0 && j >= k) || e < 0 || e >= E) continue;
     const uint32_t *c = col + e * kPermWords;
     int rank = __popc(c[word] & below);
     for (int w = 0; w < word; ++w) rank += __popc(c[w]);
@@ -194,23 +237,31 @@ hipError_t launch_permute(const int32_t *topk_idx, int T, int E, int k, int32_t 
   uint32_t *bits = (uint32_t *)ws;
   int32_t *blk_count = (int32_t *)((char *)ws + nb);
   int32_t *blk_base = (int32_t *)((char *)ws + nb + nc);
+  // k = 4 or 8 with 16-byte aligned rows: vector reads of the choices
+  const bool vec = ((uintptr_t)topk_idx & 15) == 0;
+  const int kt = vec && (k == 4 || k == 8) ? k : 0;
+#define MOE_PERM_K(KERNEL, ...)                                             \
+  (kt == 8 ? KERNEL<8> __VA_ARGS__ : kt == 4 ? KERNEL<4> __VA_ARGS__ : KERNEL<0> __VA_ARGS__)
   if (nblk == 1) {
     const size_t lds = (size_t)E * kPermWords * sizeof(uint32_t) + 1024 * sizeof(int32_t);
-    perm_single_kernel<<<1, 256, lds, stream>>>(topk_idx, T, E, k, counts, offsets, sorted_src,
-                                                dest);
+    MOE_PERM_K(perm_single_kernel, <<<1, 256, lds, stream>>>(topk_idx, T, E, k, counts, offsets,
+                                                             sorted_src, dest));
     return hipGetLastError();
   }
   if (nblk > 0) {
-    perm_count_kernel<<<nblk, 256, (size_t)E * kPermWords * sizeof(uint32_t), stream>>>(
-        topk_idx, T, E, k, bits, blk_count);
+    MOE_PERM_K(perm_count_kernel,
+               <<<nblk, 256, (size_t)E * kPermWords * sizeof(uint32_t), stream>>>(
+                   topk_idx, T, E, k, bits, blk_count));
     hipError_t err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   perm_scan_kernel<<<1, 256, 0, stream>>>(blk_count, nblk, E, blk_base, counts, offsets);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
-  perm_scatter_kernel<<<nblk, 256, (size_t)E * (kPermWords + 1) * sizeof(uint32_t), stream>>>(
-      topk_idx, T, E, k, bits, blk_base, offsets, sorted_src, dest);
+  MOE_PERM_K(perm_scatter_kernel,
+             <<<nblk, 256, (size_t)E * (kPermWords + 1) * sizeof(uint32_t), stream>>>(
+                 topk_idx, T, E, k, bits, blk_base, offsets, sorted_src, dest));
+#undef MOE_PERM_K
   return hipGetLastError();
 }
 

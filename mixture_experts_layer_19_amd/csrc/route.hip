@@ -305,30 +305,35 @@ __global__ __launch_bounds__(256) void router_topk_kernel(const float *__restric
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T) return;
+  // z = bias + the K slices in order (fp64).  The slices of all NPL logits
+  // of the lane are read eight at a time before any is added, so up to
+  // 8 NPL loads are in flight (lanes past E read expert E - 1 and drop it).
+  const size_t stride = (size_t)T * E;
+  double zd[NPL];
+#pragma unroll
+  for (int i = 0; i < NPL; ++i) {
+    const int e = min(lane + 64 * i, E - 1);
+    zd[i] = bias ? (double)bias[e] : 0.0;
+  }
+  for (int ks0 = 0; ks0 < ksn; ks0 += 8) {
+    float a[NPL][8];
+#pragma unroll
+    for (int i = 0; i < NPL; ++i) {
+      const float *pe = part + (size_t)t * E + min(lane + 64 * i, E - 1);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) a[i][u] = pe[(size_t)min(ks0 + u, ksn - 1) * stride];
+    }
+#pragma unroll
+    for (int i = 0; i < NPL; ++i)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        if (ks0 + u < ksn) zd[i] += (double)a[i][u];
+  }
   float s[NPL];
 #pragma unroll
   for (int i = 0; i < NPL; ++i) {
-    int e = lane + 64 * i;
-    if (e < E) {
-      // the slices in order, four loads in flight at a time
-      const float *pe = part + (size_t)t * E + e;
-      const size_t stride = (size_t)T * E;
-      double zd = bias ? (double)bias[e] : 0.0;
-      int ks = 0;
-      for (; ks + 4 <= ksn; ks += 4) {
-        const float a0 = pe[ks * stride], a1 = pe[(ks + 1) * stride];
-        const float a2 = pe[(ks + 2) * stride], a3 = pe[(ks + 3) * stride];
-        zd += (double)a0;
-        zd += (double)a1;
-        zd += (double)a2;
-        zd += (double)a3;
-      }
-      for (; ks < ksn; ++ks) zd += (double)pe[ks * stride];
-      const float z = (float)zd;
-      s[i] = (float)(1.0 / (1.0 + exp(-(double)z)));
-    } else {
-      s[i] = -INFINITY;
-    }
+    const float z = (float)zd[i];
+    s[i] = lane + 64 * i < E ? (float)(1.0 / (1.0 + exp(-(double)z))) : -INFINITY;
   }
   unsigned taken = 0;      // bit i: s[i] already selected
   float sel_s = 0.0f;      // lane j < k keeps the j-th selection

@@ -183,6 +183,34 @@ def test_permute_bit_exact(orc, ctx, name, T):
     assert int(oc.sum()) == P
 
 
+@pytest.mark.parametrize("k,E,T,misalign", [(6, 40, 200, False), (3, 17, 700, False),
+                                            (8, 192, 100, True), (8, 192, 600, True),
+                                            (16, 64, 300, False)])
+def test_permute_other_k_and_layouts(orc, ctx, k, E, T, misalign):
+    # k read at run time (not 4 or 8), and expert choices at an address that
+    # is not 16-byte aligned (read one by one), in one block and in several
+    w = I.Workload("perm", T=T, H=256, E=E, k=k, I=128, Is=128, dtype="bf16")
+    d = desc_for(w)
+    idx = I.random_topk(w, T, tag=5)
+    P = T * k
+    flat = torch.zeros(P + 4, dtype=torch.int32, device="cuda")
+    view = flat[1:1 + P] if misalign else flat[:P]
+    view.copy_(torch.from_numpy(idx.reshape(-1)).cuda())
+    counts = torch.empty(E, dtype=torch.int32, device="cuda")
+    offs = torch.empty(E + 1, dtype=torch.int32, device="cuda")
+    src = torch.full((P,), -1, dtype=torch.int32, device="cuda")
+    dst = torch.full((P,), -1, dtype=torch.int32, device="cuda")
+    n = B.moe_workspace_bytes(d, T, B.MOE_WS_PERMUTE)
+    ws = torch.empty(n, dtype=torch.uint8, device="cuda")
+    B.moe_permute(ctx, d, view, T, counts, offs, src, dst, ws, n)
+    torch.cuda.synchronize()
+    oc, oo, os_, od = orc.permute(idx, E)
+    np.testing.assert_array_equal(counts.cpu().numpy(), oc)
+    np.testing.assert_array_equal(offs.cpu().numpy(), oo)
+    np.testing.assert_array_equal(src.cpu().numpy(), os_)
+    np.testing.assert_array_equal(dst.cpu().numpy(), od)
+
+
 def test_permute_skewed_counts(orc, ctx):
     # every token picks experts 0..k-1: one huge segment per expert, rest empty
     w = I.workload("hy4_skew", T=1000)
