@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
       for (int i = 0; i < MB; ++i) acc[n][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    auto load = [&](SkinnyBuf<F, NW, MB> &bf, int kc) {
+    auto load = [&](SkinnyBuf<F, NW, MB> &bf, int kc) MOE_INLINE {
 #pragma unroll
       for (int n = 0; n < NW; ++n)
 #pragma unroll
@@ -252,7 +252,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
         for (int i = 0; i < MB; ++i) bf.ts[i] = 0;
       }
     };
-    auto compute = [&](const SkinnyBuf<F, NW, MB> &bf) {
+    auto compute = [&](const SkinnyBuf<F, NW, MB> &bf) MOE_INLINE {
 #pragma unroll
       for (int n = 0; n < NW; ++n)
 #pragma unroll
@@ -511,7 +511,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
 
   i32x4 treg[TLD];
   uint32_t tsreg[TSL];
-  auto load_tokens = [&](int s) {
+  auto load_tokens = [&](int s) MOE_INLINE {
     const int kc = s >> 1, h = s & 1;
 #pragma unroll
     for (int i = 0; i < TLD; ++i)
@@ -522,7 +522,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
         tsreg[i] = __builtin_amdgcn_raw_buffer_load_b8(tsrs, (int)tsvoff[i], 8 * kc + 4 * h, 0);
     }
   };
-  auto store_tokens = [&](int s) {
+  auto store_tokens = [&](int s) MOE_INLINE {
     uint8_t *base = tbuf(s & 1);
 #pragma unroll
     for (int i = 0; i < TLD; ++i) *(i32x4 *)(base + tdst[i]) = treg[i];
@@ -540,7 +540,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
   constexpr int NSET = WPF + 1;
   Frag<F> wr[NSET][NBW];
   uint32_t wsr[NSET][NBW];
-  auto load_weights = [&](int s, int set) {
+  auto load_weights = [&](int s, int set) MOE_INLINE {
     const int kc = s >> 1, h = s & 1;
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
@@ -576,7 +576,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
   // read, which every wave has finished with at that stage's barrier.
   // One stage: set and slot (the register set of its weights, the LDS slot
   // of its tokens) are compile-time constants.
-  auto stage = [&](int s, auto set_c, auto slot_c) {
+  auto stage = [&](int s, auto set_c, auto slot_c) MOE_INLINE {
     constexpr int set = decltype(set_c)::value, slot = decltype(slot_c)::value;
     load_weights(min(s + WPF, nstage - 1), (set + WPF) % NSET);
     __builtin_amdgcn_sched_barrier(0);
@@ -585,7 +585,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     // use them, so the LDS latency overlaps the matrix work
     Frag<F> tf[2];
     uint32_t tsf[2];
-    auto read_frag = [&](int m, int b) {
+    auto read_frag = [&](int m, int b) MOE_INLINE {
       const uint8_t *p = base + m * 2048;
       tf[b] = make_frag<F>(*(const i32x4 *)(p + tslot(lane & 15, lane >> 4, 0) * 16),
                            *(const i32x4 *)(p + 1024 + tslot(lane & 15, lane >> 4, 1) * 16));
@@ -621,13 +621,13 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
   // stages in periods of P = lcm(NSET, 2) (slot = s % 2) so that set and
   // slot are constants; the last nstage % P stages follow the loop
   constexpr int P = (NSET % 2 == 0) ? NSET : 2 * NSET;
-  auto stage_q = [&](int s, auto q) {
+  auto stage_q = [&](int s, auto q) MOE_INLINE {
     constexpr int Q = decltype(q)::value;
     stage(s, std::integral_constant<int, Q % NSET>{}, std::integral_constant<int, Q % 2>{});
   };
   int s0 = 0;
-  for (; s0 + P <= nstage; s0 += P) static_for<P>([&](auto q) { stage_q(s0 + q.value, q); });
-  static_for<P - 1>([&](auto q) {
+  for (; s0 + P <= nstage; s0 += P) static_for<P>([&](auto q) MOE_INLINE { stage_q(s0 + q.value, q); });
+  static_for<P - 1>([&](auto q) MOE_INLINE {
     if (s0 + q.value < nstage) stage_q(s0 + q.value, q);
   });
 

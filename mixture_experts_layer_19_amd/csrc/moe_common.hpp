@@ -111,6 +111,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 
 // ----------------------------------------------------------------------------- wave helpers
 
+// For the lambdas that make up a kernel's main loop: they must be inlined
+// (a call would move the accumulators they capture to scratch memory), and
+// a large stage can exceed the inliner's cost threshold.
+#define MOE_INLINE __attribute__((always_inline))
+
 // f(std::integral_constant<int, 0>{}) ... f(std::integral_constant<int, N - 1>{})
 template <typename Fn, int... Q>
 __device__ __forceinline__ void static_for_impl(Fn &&f, std::integer_sequence<int, Q...>) {

@@ -201,17 +201,17 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
     tdst[i] = (rl >> 4) * 2048 + (seg >> 2) * 1024 + tslot(rl & 15, seg & 3, seg >> 2) * 16;
   }
   i32x4 treg[TLD];
-  auto load_tokens = [&](int s) {
+  auto load_tokens = [&](int s) MOE_INLINE {
 #pragma unroll
     for (int i = 0; i < TLD; ++i) treg[i] = *(const i32x4 *)(tsrc[i] + s * 128);
   };
-  auto store_tokens = [&](uint8_t *buf) {
+  auto store_tokens = [&](uint8_t *buf) MOE_INLINE {
 #pragma unroll
     for (int i = 0; i < TLD; ++i) *(i32x4 *)(buf + tdst[i]) = treg[i];
   };
   // weight fragments of one stage: [term][pp]
   i32x4 wr[NSET][3][2];
-  auto load_weights = [&](int s, int set) {
+  auto load_weights = [&](int s, int set) MOE_INLINE {
 #pragma unroll
     for (int term = 0; term < 3; ++term)
 #pragma unroll
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
   for (int m = 0; m < MBT; ++m) acc[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   // stage s: weights in register set `set`, tokens in LDS slot `slot`
-  auto stage = [&](int s, auto set_c, auto slot_c) {
+  auto stage = [&](int s, auto set_c, auto slot_c) MOE_INLINE {
     constexpr int set = decltype(set_c)::value, slot = decltype(slot_c)::value;
     load_weights(min(s + WPF, s_end - 1), (set + WPF) % NSET);
     const uint8_t *base = slot ? tb1 : tb0;
@@ -259,13 +259,13 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
   __syncthreads();
   // periods of P = lcm(NSET, 2) stages keep set and slot compile-time
   constexpr int P = (NSET % 2 == 0) ? NSET : 2 * NSET;
-  auto stage_q = [&](int s, auto q) {
+  auto stage_q = [&](int s, auto q) MOE_INLINE {
     constexpr int Q = decltype(q)::value;
     stage(s, std::integral_constant<int, Q % NSET>{}, std::integral_constant<int, Q % 2>{});
   };
   int s = s_begin;
-  for (; s + P <= s_end; s += P) static_for<P>([&](auto q) { stage_q(s + q.value, q); });
-  static_for<P - 1>([&](auto q) {
+  for (; s + P <= s_end; s += P) static_for<P>([&](auto q) MOE_INLINE { stage_q(s + q.value, q); });
+  static_for<P - 1>([&](auto q) MOE_INLINE {
     if (s + q.value < s_end) stage_q(s + q.value, q);
   });
 
