@@ -43,6 +43,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip timing the batch replayed from a captured HIP graph")
     ap.add_argument("--single-stream", action="store_true",
                     help="run the shared expert on the main stream (per-stage times then "
                          "measure each kernel alone)")
@@ -122,6 +124,25 @@ def main():
         wall = (time.perf_counter() - h0) * 1e3
         return e0.elapsed_time(e1) / steps, wall / steps, out
 
+    def run_graph(x_dev, T, steps, warmup):
+        # the same forward captured once as a HIP graph and replayed on the
+        # caller's stream: what a serving loop that records its decode step
+        # would run
+        out = torch.empty((T, w.H), dtype=lay.out_dtype(), device=dev)
+        xs = x_dev.clone()
+        graph = lay.capture(xs, out)
+        for _ in range(warmup):
+            graph.replay()
+        torch.cuda.synchronize(dev)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(main_stream)
+        for _ in range(steps):
+            graph.replay()
+        e1.record(main_stream)
+        torch.cuda.synchronize(dev)
+        return e0.elapsed_time(e1) / steps
+
     def stage_profile(x_dev, T, steps):
         B.moe_ctx_set_profiling(lay.ctx, True)
         out = torch.empty((T, w.H), dtype=lay.out_dtype(), device=dev)
@@ -195,6 +216,12 @@ def main():
                   "host_wall_ms_per_step": round(wall_ms, 4)},
         "stages_ms": {k: round(v, 4) for k, v in stages.items()},
     }
+    if not a.no_graph:
+        gms = run_graph(xd, T, a.steps, a.warmup)
+        result["graph_replay"] = {"ms_per_step": round(gms, 4),
+                                  "tokens_per_s": round(T / (gms * 1e-3), 1),
+                                  "hbm_frac": round(layer_bytes / (gms * 1e-3) / 1e9
+                                                    / HBM_PEAK_GBPS, 4)}
 
     # ------------------------------------------------------------------ prefill batch
     if not a.no_prefill and w.name == "hy3_decode":

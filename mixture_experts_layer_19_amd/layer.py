@@ -128,6 +128,24 @@ class DeviceLayer:
         B.moe_layer_forward(self.ctx, self.desc, self.weights, x, T, out, ws, ws.numel(), s)
         return out
 
+    def capture(self, x: torch.Tensor, out: torch.Tensor):
+        """Record one forward of the layer (x -> out, this layer's workspace)
+        as a HIP graph and return it; ``graph.replay()`` runs the same kernels
+        again on whatever x holds then.  The side stream joins the capture at
+        the input-ready event and leaves it at the shared-done event, as in an
+        eager call, so the graph keeps the two-stream schedule.  Nothing in
+        the forward path allocates, clears memory or synchronizes, which is
+        what capture requires."""
+        T = x.shape[0]
+        ws = self.workspace(T)
+        torch.cuda.synchronize(self.dev)
+        g = torch.cuda.CUDAGraph()
+        cs = torch.cuda.Stream(device=self.dev)
+        with torch.cuda.graph(g, stream=cs):
+            B.moe_layer_forward(self.ctx, self.desc, self.weights, x, T, out, ws, ws.numel(), cs)
+        torch.cuda.synchronize(self.dev)
+        return g
+
     def close(self):
         if self.ctx:
             torch.cuda.synchronize(self.dev)

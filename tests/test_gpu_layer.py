@@ -125,6 +125,28 @@ def test_layer_is_deterministic_and_stream_independent(name):
     assert torch.equal(a, c)
 
 
+@pytest.mark.parametrize("name", ["tiny", "hy3_decode"])
+def test_layer_graph_replay_matches_eager(name):
+    # one forward captured as a HIP graph (both streams), replayed on new
+    # inputs with eager calls and synchronizations in between: every replay
+    # must equal the eager result for the same input bit for bit
+    w = I.workload(name)
+    lay = device_layer(w)
+    x0 = to_device(I.x_input(w)[0])
+    xs = [x0, torch.flip(x0, [0]).contiguous(), x0 * 0.5]   # three different batches
+    x_static = xs[0].clone()
+    out_static = torch.empty((w.T, w.H), dtype=lay.out_dtype(), device="cuda")
+    graph = lay.capture(x_static, out_static)
+    for rep in range(6):
+        xin = xs[rep % 3]
+        eager = lay.forward(xin).clone()          # eager work between replays
+        torch.cuda.synchronize()
+        x_static.copy_(xin)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_static, eager), "replay %d differs from the eager call" % rep
+
+
 def test_layer_workspace_too_small():
     w = I.workload("tiny")
     lay = device_layer(w)
