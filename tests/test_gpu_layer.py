@@ -47,8 +47,9 @@ def _sample_tokens(w, o_idx_all=None, n_rand=16):
     return np.array(sorted(toks))
 
 
-def _check_layer(orc, name, T=None, full=False):
-    w = I.workload(name) if T is None else I.workload(name, T=T)
+def _check_layer(orc, name, T=None, full=False, w=None):
+    if w is None:
+        w = I.workload(name) if T is None else I.workload(name, T=T)
     lay = device_layer(w)
     x, xd, out, g_idx = _gpu_forward(lay, w, w.T)
     assert np.isfinite(out).all()
@@ -94,6 +95,17 @@ def test_layer_mx_sampled(orc):
 @pytest.mark.parametrize("T", [1, 5, 77, 300])
 def test_layer_ragged_token_counts(orc, T):
     _check_layer(orc, "hy3_decode", T=T, full=T <= 77)
+
+
+@pytest.mark.parametrize("dtype,E,k,T", [("bf16", 1024, 16, 300), ("f32", 1024, 16, 70),
+                                         ("bf16", 1024, 1, 260), ("mxfp8", 1024, 16, 40)])
+def test_layer_largest_expert_count_and_top_k(orc, dtype, E, k, T):
+    # the largest E and k the library accepts (1024, 16), and k = 1, on a
+    # narrow layer so the oracle stays quick; every token is compared.  MX
+    # needs hidden and intermediate sizes in whole 256-element chunks.
+    H, Iw = (512, 256) if dtype == "mxfp8" else (256, 128)
+    w = I.Workload("maxes", T=T, H=H, E=E, k=k, I=Iw, Is=Iw, dtype=dtype)
+    _check_layer(orc, "maxes", w=w, full=True)
 
 
 def test_layer_zero_tokens_is_a_noop():
