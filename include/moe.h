@@ -25,7 +25,8 @@
  *    results are ready when that stream reaches the point of the call.
  *  - Arguments are validated before anything is enqueued.  A failed validation
  *    returns MOE_ERR_INVALID_ARG / MOE_ERR_UNSUPPORTED / MOE_ERR_WORKSPACE and
- *    enqueues nothing.  T == 0 returns MOE_OK and enqueues nothing.  A HIP
+ *    enqueues nothing.  T == 0 returns MOE_OK and enqueues nothing; T * top_k
+ *    above 2^31 - 1 (the int32 pair indices) returns MOE_ERR_UNSUPPORTED.  A HIP
  *    launch error returns MOE_ERR_DEVICE (text in moe_ctx_last_error).  Faults
  *    inside kernels surface at the caller's next synchronisation, as with any
  *    HIP library.  No call aborts or throws.

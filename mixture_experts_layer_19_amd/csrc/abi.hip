@@ -61,6 +61,12 @@ moe_status check_desc(const moe_desc *d) {
   return MOE_OK;
 }
 
+// Rows of the routed GEMMs and (token, slot) pair indices are int32: T * k
+// must stay below 2^31.
+bool too_many_pairs(const moe_desc *d, int32_t T) {
+  return (long long)T * d->top_k > (long long)INT32_MAX;
+}
+
 // Layout of one call's workspace.  All offsets 256-byte aligned.
 struct Layout {
   size_t logits, idx, w, counts, offsets, src, dest, perm, xq, xs, h, hs, sh_h, sh_hs, y, z, total;
@@ -309,7 +315,9 @@ moe_status moe_ctx_stage_ms(moe_ctx *ctx, float *ms) {
 }
 
 size_t moe_workspace_bytes(const moe_desc *desc, int32_t T, int which) {
-  if (check_desc(desc) != MOE_OK || T < 0 || which < MOE_WS_ROUTE || which > MOE_WS_LAYER) return 0;
+  if (check_desc(desc) != MOE_OK || T < 0 || too_many_pairs(desc, T) || which < MOE_WS_ROUTE ||
+      which > MOE_WS_LAYER)
+    return 0;
   return layout(desc, T, which).total;
 }
 
@@ -369,6 +377,7 @@ moe_status moe_route(moe_ctx *ctx, const moe_desc *desc, const void *x, int32_t 
   if (st != MOE_OK) return st;
   if ((st = check_ctx(ctx)) != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !router_w || !topk_idx || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
   Layout L = layout(desc, T, MOE_WS_ROUTE);
@@ -387,6 +396,7 @@ moe_status moe_permute(moe_ctx *ctx, const moe_desc *desc, const int32_t *topk_i
   if (st != MOE_OK) return st;
   if ((st = check_ctx(ctx)) != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!topk_idx || !expert_counts || !expert_offsets || !sorted_src || !dest || !ws)
     return MOE_ERR_INVALID_ARG;
@@ -407,6 +417,7 @@ moe_status moe_grouped_ffn(moe_ctx *ctx, const moe_desc *desc, const moe_weights
   if ((st = check_ctx(ctx)) != MOE_OK) return st;
   if (shared != 0 && shared != 1) return MOE_ERR_INVALID_ARG;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0 || (shared && desc->shared_inter == 0)) return MOE_OK;
   if (!x || !y || !ws || !weights_ok(desc, w, 0, !shared, shared)) return MOE_ERR_INVALID_ARG;
   if (!shared && (!sorted_src || !expert_offsets)) return MOE_ERR_INVALID_ARG;
@@ -438,6 +449,7 @@ moe_status moe_combine(moe_ctx *ctx, const moe_desc *desc, const void *y, const 
   if (st != MOE_OK) return st;
   if ((st = check_ctx(ctx)) != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y || !dest || !topk_w || !out) return MOE_ERR_INVALID_ARG;
   const int of = fmt_of(desc->out_dtype);
@@ -451,6 +463,7 @@ moe_status moe_layer_ws_topk(const moe_desc *desc, int32_t T, size_t *idx_offset
   moe_status st = check_desc(desc);
   if (st != MOE_OK) return st;
   if (T < 0 || !idx_offset || !w_offset) return MOE_ERR_INVALID_ARG;
+  if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   Layout L = layout(desc, T, MOE_WS_LAYER);
   *idx_offset = L.idx;
   *w_offset = L.w;
@@ -464,6 +477,7 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   if (st != MOE_OK) return st;
   if ((st = check_ctx(ctx)) != MOE_OK) return st;
   if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !out || !ws || !weights_ok(desc, w, 1, 1, 1)) return MOE_ERR_INVALID_ARG;
   Layout L = layout(desc, T, MOE_WS_LAYER);

@@ -78,6 +78,17 @@ def test_workspace_and_packed_sizes(B):
     assert i0 != w0
 
 
+def test_token_pairs_beyond_int32_are_rejected(B):
+    # (token, slot) pairs are int32 indices: T * k must stay below 2^31
+    d = _desc(B)                                   # k = 8
+    T_ok = (2 ** 31 - 1) // 8
+    assert B.moe_workspace_bytes(d, T_ok, B.MOE_WS_PERMUTE) > 0
+    assert B.moe_workspace_bytes(d, T_ok + 1, B.MOE_WS_PERMUTE) == 0
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_layer_ws_topk(d, T_ok + 1)
+    assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+
+
 @pytest.mark.parametrize("bad", [dict(top_k=0), dict(top_k=17), dict(num_experts=2000),
                                  dict(top_k=9, num_experts=8), dict(hidden=100),
                                  dict(inter=100), dict(route_norm=3), dict(act_dtype=7)])
