@@ -65,6 +65,12 @@ def _load():
         lib.oracle_e4m3_encode.argtypes = [ctypes.c_double]
         lib.oracle_mxq.argtypes = [I64, P, P, P]
         lib.oracle_mx_dequant.argtypes = [I64, P, P, P]
+        lib.oracle_e2m1_decode.restype = ctypes.c_double
+        lib.oracle_e2m1_decode.argtypes = [ctypes.c_uint8]
+        lib.oracle_e2m1_encode.restype = ctypes.c_uint8
+        lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
+        lib.oracle_mxq4.argtypes = [I64, P, P, P]
+        lib.oracle_mx4_dequant.argtypes = [I64, P, P, P]
         lib.oracle_router_logits.argtypes = [I64, I64, I64, P, P, P, P]
         lib.oracle_route.argtypes = [I64, I64, I64, I64, P, P, P, ctypes.c_float, ctypes.c_int,
                                      P, P, P, P]
@@ -75,7 +81,8 @@ def _load():
         lib.oracle_layer_forward.argtypes = (
             [I64, I64, I64, I64, I64, I64, ctypes.c_float, ctypes.c_int, P, P, P, ctypes.c_int]
             + [P] * 6 + [ctypes.c_int] + [P] * 10)
-        for name in ("oracle_mxq", "oracle_mx_dequant", "oracle_router_logits", "oracle_route",
+        for name in ("oracle_mxq", "oracle_mx_dequant", "oracle_mxq4", "oracle_mx4_dequant",
+                     "oracle_router_logits", "oracle_route",
                      "oracle_permute", "oracle_swiglu_rows", "oracle_combine",
                      "oracle_layer_forward"):
             getattr(lib, name).restype = ctypes.c_int
@@ -145,6 +152,49 @@ def mx_dequant(q, s):
     return v
 
 
+# ----------------------------------------------------------------------------- MXFP4
+
+# MX modes of the FFN and layer functions: none, MX-fp8 experts and
+# activations (W8A8), MXFP4 routed experts with MX-fp8 activations (W4A8;
+# the shared expert stays W8A8)
+MX_NONE, MX_FP8, MX_W4A8 = 0, 1, 2
+
+
+def e2m1_decode(code: int) -> float:
+    return _load().oracle_e2m1_decode(int(code))
+
+
+def e2m1_encode(v: float) -> int:
+    return int(_load().oracle_e2m1_encode(float(v)))
+
+
+def mxq4(v):
+    """MXFP4 quantisation along the last axis (length a multiple of 32).
+    Returns (codes uint8 in 0..15, one per element; scales uint8, last axis / 32)."""
+    v = _f32(v)
+    if v.shape[-1] % 32:
+        raise ValueError("last axis must be a multiple of 32")
+    q = np.empty(v.shape, np.uint8)
+    s = np.empty(v.shape[:-1] + (v.shape[-1] // 32,), np.uint8)
+    _check(_load().oracle_mxq4(v.size // 32, _p(v), _p(q), _p(s)), "mxq4")
+    return q, s
+
+
+def mx4_dequant(q, s):
+    q = np.ascontiguousarray(q, dtype=np.uint8)
+    s = np.ascontiguousarray(s, dtype=np.uint8)
+    v = np.empty(q.shape, np.float32)
+    _check(_load().oracle_mx4_dequant(q.size // 32, _p(q), _p(s), _p(v)), "mx4_dequant")
+    return v
+
+
+def _mx_mode(mx) -> int:
+    m = int(mx)
+    if m not in (MX_NONE, MX_FP8, MX_W4A8):
+        raise ValueError("mx must be 0 (none), 1 (MX-fp8) or 2 (W4A8)")
+    return m
+
+
 # ----------------------------------------------------------------------------- stages
 
 
@@ -188,7 +238,8 @@ def permute(topk_idx, E):
 
 
 def swiglu_rows(xrows, Wg, Wu, Wd, mx=False):
-    """One expert's SwiGLU FFN over rows.  Returns (h [M,I] pre-MX, y [M,H])."""
+    """One expert's SwiGLU FFN over rows.  Returns (h [M,I] pre-MX, y [M,H]).
+    mx: 0/False none, 1/True MX-fp8 (W8A8), 2 W4A8 (MXFP4 weights)."""
     xrows = _f32(xrows)
     M, H = xrows.shape
     Wg, dt = _weights(Wg)
@@ -199,7 +250,7 @@ def swiglu_rows(xrows, Wg, Wu, Wd, mx=False):
     I = Wg.shape[0]
     h = np.empty((M, I), np.float32)
     y = np.empty((M, H), np.float32)
-    _check(_load().oracle_swiglu_rows(M, H, I, _p(xrows), dt, _p(Wg), _p(Wu), _p(Wd), int(bool(mx)),
+    _check(_load().oracle_swiglu_rows(M, H, I, _p(xrows), dt, _p(Wg), _p(Wu), _p(Wd), _mx_mode(mx),
                                       _p(h), _p(y)), "swiglu_rows")
     return h, y
 
@@ -244,7 +295,7 @@ def layer_forward(x, Wr, bias, Wg, Wu, Wd, Sg=None, Su=None, Sd=None, *, k, rho,
              y=np.empty((P, H), np.float32), zsh=np.zeros((T, H), np.float32))
     _check(_load().oracle_layer_forward(
         T, H, E, k, I, Is, ctypes.c_float(rho), int(bool(route_norm)), _p(x), _p(Wr), _p(b), dt,
-        _p(Wg), _p(Wu), _p(Wd), _p(Sg), _p(Su), _p(Sd), int(bool(mx)), _p(r["out"]),
+        _p(Wg), _p(Wu), _p(Wd), _p(Sg), _p(Su), _p(Sd), _mx_mode(mx), _p(r["out"]),
         _p(r["topk_idx"]), _p(r["topk_w"]), _p(r["counts"]), _p(r["offsets"]),
         _p(r["sorted_src"]), _p(r["dest"]), _p(r["h"]), _p(r["y"]), _p(r["zsh"])),
         "layer_forward")
@@ -277,7 +328,8 @@ def layer_forward_tokens(tokens, x, Wr, bias, expert_weights, shared_weights, *,
             yk[i, j] = yr
     zsh = None
     if shared_weights is not None:
-        _, zsh = swiglu_rows(xs, *shared_weights, mx=mx)
+        # the shared expert of a W4A8 layer stays W8A8
+        _, zsh = swiglu_rows(xs, *shared_weights, mx=MX_FP8 if _mx_mode(mx) == MX_W4A8 else mx)
     # Rows of yk are already in (token, slot) order, so dest is the identity.
     dest = np.arange(n * k, dtype=np.int32)
     out = combine(yk.reshape(n * k, H), dest, w, zsh)

@@ -20,6 +20,9 @@
  *     [out, in] (a reading: the pages give only the sizes).
  *   - MX-fp8: OCP Microscaling Formats (MX) v1.0 specification, 32-element
  *     blocks, E8M0 shared scale, E4M3 (FN variant) elements.
+ *   - MXFP4 (W4A8 routed experts, Hy3 guide section 8.2): the same
+ *     specification's E2M1 elements with the same 32-element E8M0 blocks;
+ *     activations stay MX-fp8 and the shared expert stays W8A8.
  *
  * Numerics.  Every stage boundary is stored as fp32.  Every dot product and
  * every sum accumulates in double in ascending index order and is rounded
@@ -142,6 +145,93 @@ static void mx_roundtrip_row(int64_t n, const float *in, float *out) {
   for (int64_t b = 0; b < n / 32; ++b) {
     oracle_mxq(1, in + b * 32, q, &s);
     oracle_mx_dequant(1, q, &s, out + b * 32);
+  }
+}
+
+/* ------------------------------------------------------------------ */
+/* OCP MX: E2M1 (FP4) element format, for the W4A8 expert weights       */
+/* ------------------------------------------------------------------ */
+
+/* E2M1 value of a 4-bit code (OCP MX v1.0, element format table): bit 3 is
+ * the sign, bits 2-1 the exponent field (bias 1), bit 0 the mantissa; an
+ * exponent field of 0 is subnormal (m/2 * 2^0).  No infinities, no NaN.  The
+ * eight magnitudes are 0, 0.5, 1, 1.5, 2, 3, 4 and 6. */
+ORC_EXPORT double oracle_e2m1_decode(uint8_t code) {
+  int sign = (code >> 3) & 1;
+  int ef = (code >> 1) & 3;
+  int mf = code & 1;
+  double mag = (ef == 0) ? 0.5 * mf : ldexp(1.0 + 0.5 * mf, ef - 1);
+  return sign ? -mag : mag;
+}
+
+/* Round v to E2M1: the nearest of the eight magnitudes; a value exactly
+ * between two of them goes to the one whose code has mantissa bit 0 (round
+ * to nearest even); values beyond 6 become 6 (saturation, the nearest
+ * magnitude).  The sign bit is copied from v. */
+ORC_EXPORT uint8_t oracle_e2m1_encode(double v) {
+  uint8_t sign = signbit(v) ? 0x8 : 0x0;
+  double a = fabs(v);
+  /* saturate first: far above 6 every distance rounds to the same double */
+  if (a >= 6.0) return sign | 0x7;
+  int best = 0;
+  double best_d = INFINITY;
+  for (int c = 0; c < 8; ++c) {
+    double d = fabs(a - oracle_e2m1_decode((uint8_t)c));
+    /* codes ascend in magnitude, so a tie is between c - 1 and c */
+    if (d < best_d || (d == best_d && (c & 1) == 0)) {
+      best = c;
+      best_d = d;
+    }
+  }
+  return sign | (uint8_t)best;
+}
+
+/* Quantise nblk blocks of 32 fp32 values to MXFP4, one code per output
+ * byte (values 0..15).  Scale rule as for MX-fp8 with E2M1's largest normal
+ * exponent: X = floor(log2(max|v|)) - 2 (6 = 1.5 * 2^2), clamped to
+ * [-127, 127]; an all-zero block takes X = -127.  Element i is the E2M1
+ * rounding of v_i / 2^X; the scale byte is X + 127. */
+ORC_EXPORT int oracle_mxq4(int64_t nblk, const float *v, uint8_t *q, uint8_t *scale) {
+  if (nblk < 0 || (nblk > 0 && (!v || !q || !scale))) return -1;
+  for (int64_t b = 0; b < nblk; ++b) {
+    const float *vb = v + b * 32;
+    double amax = 0.0;
+    for (int i = 0; i < 32; ++i) {
+      double a = fabs((double)vb[i]);
+      if (a > amax) amax = a;
+    }
+    int X;
+    if (amax == 0.0) {
+      X = -127;
+    } else {
+      int e2;
+      frexp(amax, &e2);
+      X = (e2 - 1) - 2;
+      if (X < -127) X = -127;
+      if (X > 127) X = 127;
+    }
+    scale[b] = (uint8_t)(X + 127);
+    for (int i = 0; i < 32; ++i) q[b * 32 + i] = oracle_e2m1_encode(ldexp((double)vb[i], -X));
+  }
+  return 0;
+}
+
+/* Dequantise MXFP4: v = E2M1(q) * 2^(scale - 127). */
+ORC_EXPORT int oracle_mx4_dequant(int64_t nblk, const uint8_t *q, const uint8_t *scale, float *v) {
+  if (nblk < 0 || (nblk > 0 && (!v || !q || !scale))) return -1;
+  for (int64_t b = 0; b < nblk; ++b)
+    for (int i = 0; i < 32; ++i)
+      v[b * 32 + i] =
+          (float)ldexp(oracle_e2m1_decode(q[b * 32 + i] & 0xF), (int)scale[b] - 127);
+  return 0;
+}
+
+/* Round a row of n fp32 values through MXFP4. */
+static void mx4_roundtrip_row(int64_t n, const float *in, float *out) {
+  uint8_t q[32], s;
+  for (int64_t b = 0; b < n / 32; ++b) {
+    oracle_mxq4(1, in + b * 32, q, &s);
+    oracle_mx4_dequant(1, q, &s, out + b * 32);
   }
 }
 
@@ -291,19 +381,23 @@ ORC_EXPORT int oracle_permute(int64_t T, int64_t E, int64_t k, const int32_t *to
  *   g_i = sum_h x~_h Wg[i,h],  u_i = sum_h x~_h Wu[i,h]     (double)
  *   h_i = fp32( silu(g_i) * u_i ),  silu(g) = g / (1 + exp(-g))
  *   y_n = fp32( sum_i h~_i Wd[n,i] )
- * where x~ = x and h~ = h, except with mx = 1: x~ = MXQ(x) along H and
- * h~ = MXQ(h) along I, and the weights are MXQ'd along their reduction axis
- * (each Wg/Wu row along H, each Wd row along I) before use.
+ * where x~ = x and h~ = h, except with mx = 1 (MX-fp8, W8A8): x~ = MXQ(x)
+ * along H and h~ = MXQ(h) along I, and the weights are MXQ'd along their
+ * reduction axis (each Wg/Wu row along H, each Wd row along I) before use;
+ * and with mx = 2 (W4A8: MXFP4 weights, MX-fp8 activations) the same, except
+ * that the weights are rounded through MXFP4 instead.
  * h_out [M,I] (optional) receives h before any MX rounding; y [M,H]. */
 ORC_EXPORT int oracle_swiglu_rows(int64_t M, int64_t H, int64_t I, const float *xr, int wdtype,
                                   const void *Wg, const void *Wu, const void *Wd, int mx,
                                   float *h_out, float *y) {
   if (M < 0 || H <= 0 || I <= 0 || (wdtype != 0 && wdtype != 1)) return -1;
-  if (mx && (wdtype != 0 || H % 32 || I % 32)) return -1;
+  if (mx < 0 || mx > 2 || (mx && (wdtype != 0 || H % 32 || I % 32))) return -1;
   if (M == 0) return 0;
   if (!xr || !Wg || !Wu || !Wd || !y) return -1;
 
   /* MX: pre-round the weights once (dequantised fp32 copies). */
+  void (*wround)(int64_t, const float *, float *) = (mx == 2) ? mx4_roundtrip_row
+                                                               : mx_roundtrip_row;
   float *wg_q = NULL, *wu_q = NULL, *wd_q = NULL;
   const void *g_src = Wg, *u_src = Wu, *d_src = Wd;
   if (mx) {
@@ -313,11 +407,11 @@ ORC_EXPORT int oracle_swiglu_rows(int64_t M, int64_t H, int64_t I, const float *
     if (!wg_q || !wu_q || !wd_q) { free(wg_q); free(wu_q); free(wd_q); return -1; }
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < I; ++i) {
-      mx_roundtrip_row(H, (const float *)Wg + i * H, wg_q + i * H);
-      mx_roundtrip_row(H, (const float *)Wu + i * H, wu_q + i * H);
+      wround(H, (const float *)Wg + i * H, wg_q + i * H);
+      wround(H, (const float *)Wu + i * H, wu_q + i * H);
     }
 #pragma omp parallel for schedule(static)
-    for (int64_t n = 0; n < H; ++n) mx_roundtrip_row(I, (const float *)Wd + n * I, wd_q + n * I);
+    for (int64_t n = 0; n < H; ++n) wround(I, (const float *)Wd + n * I, wd_q + n * I);
     g_src = wg_q; u_src = wu_q; d_src = wd_q;
   }
 
@@ -398,6 +492,9 @@ ORC_EXPORT int oracle_combine(int64_t T, int64_t H, int64_t k, const float *y, c
  *   Wr [E,H] fp32, bias [E] or NULL
  *   Wg, Wu [E,I,H]; Wd [E,H,I]    (wdtype 0 fp32 / 1 bf16 bits; fp32 if mx)
  *   Sg, Su [Is,H]; Sd [H,Is]      (shared expert; NULL or Is == 0: none)
+ *   mx: 0 none, 1 MX-fp8 experts (W8A8), 2 W4A8: MXFP4 routed experts with
+ *       MX-fp8 activations, and an MX-fp8 (W8A8) shared expert -- the hybrid
+ *       recipe of the Hy3 guide, section 8.2 (routed W4A8, shared W8A8)
  * Outputs: out [T,H]; optional intermediates (any may be NULL):
  *   topk_idx [T,k], topk_w [T,k], counts [E], offsets [E+1],
  *   sorted_src [T*k], dest [T*k], h [T*k, I] (pre-MX), y [T*k, H],
@@ -451,7 +548,9 @@ ORC_EXPORT int oracle_layer_forward(int64_t T, int64_t H, int64_t E, int64_t k, 
       goto done;
   }
   /* Shared expert on every token. */
-  if (have_shared && oracle_swiglu_rows(T, H, Is, x, wdtype, Sg, Su, Sd, mx, NULL, zsh)) goto done;
+  if (have_shared &&
+      oracle_swiglu_rows(T, H, Is, x, wdtype, Sg, Su, Sd, mx == 2 ? 1 : mx, NULL, zsh))
+    goto done;
   /* FinalizeRouting + add. */
   if (oracle_combine(T, H, k, y, dest, w, zsh, out)) goto done;
 
