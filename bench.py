@@ -37,7 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="hy3_decode",
-                    choices=["hy3_decode", "hy3_prefill", "hy4_skew", "mx", "tiny"])
+                    choices=["hy3_decode", "hy3_prefill", "hy4_skew", "mx", "tiny", "w4a8_decode",
+                             "w4a8"])
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -161,8 +162,13 @@ def main():
         idx = ws[io:io + 4 * T * w.k].view(torch.int32).cpu().numpy()
         return int(np.unique(idx).size)
 
-    eb = {"bf16": 2, "f32": 4, "mxfp8": 1}[w.dtype]
-    sb = (1.0 / 32.0) if w.dtype == "mxfp8" else 0.0       # MX scale bytes per weight
+    # bytes per weight of the routed and the shared experts (MX: + one scale
+    # byte per 32); W4A8 keeps its shared expert in MX-fp8
+    mxw = w.dtype in ("mxfp8", "w4a8")
+    eb = {"bf16": 2, "f32": 4, "mxfp8": 1, "w4a8": 0.5}[w.dtype]
+    ebs = 1 if w.dtype == "w4a8" else eb
+    sb = (1.0 / 32.0) if mxw else 0.0
+    ab = 1 if mxw else eb                      # bytes per element of h
     ob = 4 if w.dtype == "f32" else 2
     xb = 4 if w.dtype == "f32" else 2
 
@@ -178,15 +184,16 @@ def main():
     # algorithmic bytes: weights of the touched experts, shared expert, router,
     # activations in, layer output
     expert_bytes = (3 * w.I * w.H) * (eb + sb)
-    shared_bytes = (3 * w.Is * w.H) * (eb + sb)
+    shared_bytes = (3 * w.Is * w.H) * (ebs + sb)
     layer_bytes = (touched * expert_bytes + shared_bytes + w.E * w.H * 4 + T * w.H * xb
                    + T * w.H * ob)
-    gu_bytes = touched * (2 * w.I * w.H) * (eb + sb) + T * w.H * xb + P * w.I * (eb + sb)
+    gu_bytes = touched * (2 * w.I * w.H) * (eb + sb) + T * w.H * xb + P * w.I * (ab + sb)
     gu_ms = stages["gate_up"]
     flops = 2.0 * P * 3 * w.I * w.H + 2.0 * T * 3 * w.Is * w.H
     gu_flops = 2.0 * P * 2 * w.I * w.H
     tok_s = T / (ms * 1e-3)
-    mfma_peak = FP8_PEAK_TFLOPS if w.dtype == "mxfp8" else BF16_PEAK_TFLOPS
+    # MX products run at the fp8 rate (an E2M1 x E4M3 product is priced as fp8)
+    mfma_peak = FP8_PEAK_TFLOPS if mxw else BF16_PEAK_TFLOPS
     if w.name == "hy3_prefill":
         roof = {"bound": "mfma", "kernel": "routed gate/up + SwiGLU grouped GEMM",
                 "achieved": round(gu_flops / (gu_ms * 1e-3) / 1e12, 1), "peak": mfma_peak,
@@ -202,7 +209,8 @@ def main():
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "mxfp8-e4m3"}[w.dtype],
+        "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "mxfp8-e4m3",
+                  "w4a8": "mxfp4-e2m1 x mxfp8-e4m3"}[w.dtype],
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": w.name, "tokens": T, "hidden": w.H, "experts": w.E,
                    "top_k": w.k, "inter": w.I, "shared_inter": w.Is,
@@ -269,7 +277,7 @@ def main():
         def oracle_tokens(toks):
             oracle.layer_forward_tokens(toks, x32, Wr, bias, lambda e: (Wg[e], Wu[e], Wd[e]),
                                         shared, k=w.k, rho=w.rho, route_norm=w.route_norm,
-                                        mx=(w.dtype == "mxfp8"))
+                                        mx={"mxfp8": 1, "w4a8": 2}.get(w.dtype, 0))
 
         # a bounded sample: the first n tokens of the batch (all of them when
         # the batch is small), evaluated `reps` times back to back

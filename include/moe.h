@@ -35,7 +35,8 @@
  *  - A moe_ctx may be used by one host thread at a time.
  *
  * Shape limits: 1 <= E <= 1024, 1 <= k <= min(E, 16); H a multiple of 256;
- * I and I_s multiples of 128 (256 for MX-fp8); I_s = 0 means no shared expert.
+ * I and I_s multiples of 128 (256 for MX-fp8 and MXFP4); I_s = 0 means no
+ * shared expert.
  */
 #ifndef MOE_H_
 #define MOE_H_
@@ -60,7 +61,9 @@ typedef enum moe_status {
 typedef enum moe_dtype {
   MOE_F32 = 0,   /* IEEE binary32                                           */
   MOE_BF16 = 1,  /* bfloat16, round-to-nearest-even on every store          */
-  MOE_MXFP8 = 2  /* OCP MX: E4M3 (FN) elements, one E8M0 scale per 32       */
+  MOE_MXFP8 = 2, /* OCP MX: E4M3 (FN) elements, one E8M0 scale per 32       */
+  MOE_MXFP4 = 3  /* OCP MX: E2M1 elements (two per byte, low nibble first),
+                    one E8M0 scale per 32; expert weights only (W4A8)      */
 } moe_dtype;
 
 /* Layer description (host struct).  Field names follow HYV3Config (Hy3 guide,
@@ -70,6 +73,11 @@ typedef enum moe_dtype {
  *   (BF16, MXFP8, BF16) MX-fp8 experts; activations x and the SwiGLU output
  *                       are quantised to MX-fp8 on the fly (32-element blocks
  *                       along the reduction axis); bf16 output
+ *   (BF16, MXFP4, BF16) W4A8, the hybrid recipe of the Hy3 guide, section 8.2:
+ *                       routed experts MXFP4 (scale X = floor(log2 max|v|) - 2,
+ *                       E2M1 round-to-nearest-even, saturating at 6), the
+ *                       shared expert MX-fp8 (W8A8), activations MX-fp8 as
+ *                       above; bf16 output
  * The router always runs in fp32 on the unquantised x. */
 typedef struct moe_desc {
   int32_t hidden;                /* H                                        */
@@ -123,7 +131,8 @@ MOE_API size_t moe_workspace_bytes(const moe_desc *desc /* host */, int32_t T, i
 
 /* Packed weight sizes in bytes.  shared: 0 routed experts, 1 shared expert.
  * which: MOE_PACK_GATE_UP, MOE_PACK_DOWN, MOE_PACK_GATE_UP_SCALE,
- * MOE_PACK_DOWN_SCALE (scales are 0 bytes unless expert_dtype is MX-fp8). */
+ * MOE_PACK_DOWN_SCALE (scales are 0 bytes unless expert_dtype is MX-fp8 or
+ * MXFP4; the shared expert of an MXFP4 layer is packed as MX-fp8). */
 enum { MOE_PACK_GATE_UP = 0, MOE_PACK_DOWN = 1, MOE_PACK_GATE_UP_SCALE = 2,
        MOE_PACK_DOWN_SCALE = 3 };
 MOE_API size_t moe_packed_bytes(const moe_desc *desc /* host */, int shared, int which);
@@ -132,11 +141,13 @@ MOE_API size_t moe_packed_bytes(const moe_desc *desc /* host */, int shared, int
  * the HunyuanImage-3.0 article, part 1, built from per-expert [out,in]
  * matrices).  Inputs, row-major, src_dtype MOE_F32 or MOE_BF16:
  *   gate [E,I,H], up [E,I,H], down [E,H,I]   (shared: E = 1, I = I_s)
- * Outputs in desc->expert_dtype: gate_up_out, down_out, and for MX-fp8 the
- * scale arrays (quantised here: OCP MX rule, blocks of 32 along the
- * reduction axis).  Sizes from moe_packed_bytes.  Layout: 4 KiB blocks of 16
- * output rows x 256 bytes of K, ordered [expert][row block][K chunk]; gate
- * and up row blocks alternate (gate block j, then up block j). */
+ * Outputs in desc->expert_dtype (MX-fp8 for the shared expert of an MXFP4
+ * layer): gate_up_out, down_out, and for MX formats the scale arrays
+ * (quantised here: OCP MX rule, blocks of 32 along the reduction axis).
+ * Sizes from moe_packed_bytes.  Layout: 4 KiB blocks of 16 output rows x 256
+ * bytes of K (MXFP4: 2 KiB blocks of 16 rows x 256 K elements), ordered
+ * [expert][row block][K chunk]; gate and up row blocks alternate (gate
+ * block j, then up block j). */
 MOE_API moe_status moe_pack_experts(const moe_desc *desc /* host */, int shared, int src_dtype,
                             const void *gate, const void *up, const void *down,
                             void *gate_up_out, void *down_out, uint8_t *gate_up_scale_out,

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIBMOE") or os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
-MOE_F32, MOE_BF16, MOE_MXFP8 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3
 MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_SHARED_FFN, MOE_WS_LAYER = range(5)
 MOE_PACK_GATE_UP, MOE_PACK_DOWN, MOE_PACK_GATE_UP_SCALE, MOE_PACK_DOWN_SCALE = range(4)
 

@@ -37,10 +37,28 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 
 int fmt_of(int dtype) {
-  return dtype == MOE_F32 ? FMT_F32 : dtype == MOE_BF16 ? FMT_BF16 : FMT_MX8;
+  return dtype == MOE_F32 ? FMT_F32
+         : dtype == MOE_BF16 ? FMT_BF16
+         : dtype == MOE_MXFP4 ? FMT_MX4 : FMT_MX8;
 }
 size_t elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1; }
 int chunk_elems(int dtype) { return dtype == MOE_F32 ? 64 : dtype == MOE_BF16 ? 128 : 256; }
+
+// Block-scaled experts: the activations x and h are MX-fp8 (W8A8 and W4A8).
+bool mx_act(const moe_desc *d) {
+  return d->expert_dtype == MOE_MXFP8 || d->expert_dtype == MOE_MXFP4;
+}
+// Kernel weight format of the routed (shared = 0) or shared experts: a W4A8
+// layer keeps its shared expert in MX-fp8 (the hybrid recipe of the Hy3 guide,
+// section 8.2: routed experts W4A8, shared expert W8A8).
+int weight_fmt(const moe_desc *d, int shared) {
+  if (d->expert_dtype == MOE_MXFP4 && shared) return FMT_MX8;
+  return fmt_of(d->expert_dtype);
+}
+// Bytes of one packed weight block (16 rows x one K chunk).
+size_t wblock(int fmt) { return fmt == FMT_MX4 ? 2048 : kBlockBytes; }
+// Bytes per activation element in the experts' input format (x, h).
+size_t act_bytes(const moe_desc *d) { return mx_act(d) ? 1 : elem_bytes(d->expert_dtype); }
 
 // Shape and dtype checks shared by every entry point.
 moe_status check_desc(const moe_desc *d) {
@@ -50,10 +68,12 @@ moe_status check_desc(const moe_desc *d) {
     return MOE_ERR_INVALID_ARG;
   if (d->route_norm != 0 && d->route_norm != 1) return MOE_ERR_INVALID_ARG;
   for (int v : {d->act_dtype, d->expert_dtype, d->out_dtype})
-    if (v < MOE_F32 || v > MOE_MXFP8) return MOE_ERR_INVALID_ARG;
+    if (v < MOE_F32 || v > MOE_MXFP4) return MOE_ERR_INVALID_ARG;
   const bool f32 = d->act_dtype == MOE_F32 && d->expert_dtype == MOE_F32 && d->out_dtype == MOE_F32;
   const bool b16 = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_BF16 && d->out_dtype == MOE_BF16;
-  const bool mx = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_MXFP8 && d->out_dtype == MOE_BF16;
+  const bool mx = d->act_dtype == MOE_BF16 && (d->expert_dtype == MOE_MXFP8 ||
+                                              d->expert_dtype == MOE_MXFP4) &&
+                  d->out_dtype == MOE_BF16;
   if (!(f32 || b16 || mx)) return MOE_ERR_UNSUPPORTED;
   // K chunks of 256 bytes; output tiles of 256 rows / 16-block groups
   const int im = mx ? 256 : 128;
@@ -77,8 +97,8 @@ Layout layout(const moe_desc *d, int T, int which) {
   memset(&L, 0, sizeof L);
   const size_t P = (size_t)T * d->top_k, E = d->num_experts, H = d->hidden;
   const size_t I = d->inter, Is = d->shared_inter;
-  const bool mx = d->expert_dtype == MOE_MXFP8;
-  const size_t eh = elem_bytes(d->expert_dtype), eo = elem_bytes(d->out_dtype);
+  const bool mx = mx_act(d);
+  const size_t eh = act_bytes(d), eo = elem_bytes(d->out_dtype);
   size_t off = 0;
   auto take = [&](size_t bytes) { size_t o = off; off += align_up(bytes); return o; };
   const bool layer = which == MOE_WS_LAYER;
@@ -148,18 +168,19 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
                hipEvent_t after_first = nullptr) {
   const int st1 = shared ? MOE_STAGE_SHARED_GATE_UP : MOE_STAGE_GATE_UP;
   const int st2 = shared ? MOE_STAGE_SHARED_DOWN : MOE_STAGE_DOWN;
-  const int F = fmt_of(d->expert_dtype);
+  const int F = weight_fmt(d, shared);
   const int H = d->hidden, I = shared ? d->shared_inter : d->inter;
   const int E = shared ? 1 : d->num_experts;
   const int rows = shared ? T : T * d->top_k;
-  const size_t eb = elem_bytes(d->expert_dtype);
+  const size_t eb = act_bytes(d);                 // token-side bytes per element
   const int ce = chunk_elems(d->expert_dtype);
+  const size_t wb = wblock(F);
 
   GemmArgs g1;
   memset(&g1, 0, sizeof g1);
   g1.w = (const uint8_t *)(shared ? w->sh_gate_up : w->gate_up);
   g1.w_scale = (const uint16_t *)(shared ? w->sh_gate_up_scale : w->gate_up_scale);
-  g1.w_expert_stride = (size_t)(2 * I / 16) * (H / ce) * kBlockBytes;
+  g1.w_expert_stride = (size_t)(2 * I / 16) * (H / ce) * wb;
   g1.ws_expert_stride = (size_t)(2 * I / 16) * (H / ce) * 64;
   g1.a = (const uint8_t *)xa;
   g1.a_scale = xs;
@@ -177,7 +198,8 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g1.n_out = I;
   hipError_t err;
   if (tm && (err = tm->start(st1, s)) != hipSuccess) return err;
-  err = launch_grouped_gemm(g1, F, EPI_SWIGLU, F, rows, s);
+  // the SwiGLU output h is the down GEMM's input: MX-fp8 for MX experts
+  err = launch_grouped_gemm(g1, F, EPI_SWIGLU, mx_act(d) ? FMT_MX8 : F, rows, s);
   if (err != hipSuccess) return err;
   if (tm && (err = tm->stop(st1, s)) != hipSuccess) return err;
   if (after_first && (err = hipEventRecord(after_first, s)) != hipSuccess) return err;
@@ -186,7 +208,7 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   memset(&g2, 0, sizeof g2);
   g2.w = (const uint8_t *)(shared ? w->sh_down : w->down);
   g2.w_scale = (const uint16_t *)(shared ? w->sh_down_scale : w->down_scale);
-  g2.w_expert_stride = (size_t)(H / 16) * (I / ce) * kBlockBytes;
+  g2.w_expert_stride = (size_t)(H / 16) * (I / ce) * wb;
   g2.ws_expert_stride = (size_t)(H / 16) * (I / ce) * 64;
   g2.a = (const uint8_t *)h;
   g2.a_scale = hs;
@@ -212,7 +234,7 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
 bool weights_ok(const moe_desc *d, const moe_weights *w, int need_router, int need_routed,
                 int need_shared) {
   if (!w) return false;
-  const bool mx = d->expert_dtype == MOE_MXFP8;
+  const bool mx = mx_act(d);
   if (need_router && !w->router_w) return false;
   if (need_routed && (!w->gate_up || !w->down || (mx && (!w->gate_up_scale || !w->down_scale))))
     return false;
@@ -325,11 +347,13 @@ size_t moe_packed_bytes(const moe_desc *desc, int shared, int which) {
   if (check_desc(desc) != MOE_OK || (shared != 0 && shared != 1)) return 0;
   const size_t E = shared ? 1 : desc->num_experts, H = desc->hidden;
   const size_t I = shared ? desc->shared_inter : desc->inter;
-  const size_t eb = elem_bytes(desc->expert_dtype);
-  const bool mx = desc->expert_dtype == MOE_MXFP8;
+  const int F = weight_fmt(desc, shared);
+  const bool mx = mx_act(desc);
+  // bytes per 32 weights (E2M1 packs two per byte)
+  const size_t per32 = F == FMT_F32 ? 128 : F == FMT_BF16 ? 64 : F == FMT_MX8 ? 32 : 16;
   switch (which) {
-    case MOE_PACK_GATE_UP: return E * 2 * I * H * eb;
-    case MOE_PACK_DOWN: return E * H * I * eb;
+    case MOE_PACK_GATE_UP: return E * 2 * I * H / 32 * per32;
+    case MOE_PACK_DOWN: return E * H * I / 32 * per32;
     case MOE_PACK_GATE_UP_SCALE: return mx ? E * 2 * I * H / 32 : 0;
     case MOE_PACK_DOWN_SCALE: return mx ? E * H * I / 32 : 0;
   }
@@ -346,10 +370,10 @@ moe_status moe_pack_experts(const moe_desc *desc, int shared, int src_dtype, con
   const int E = shared ? 1 : desc->num_experts, H = desc->hidden;
   const int I = shared ? desc->shared_inter : desc->inter;
   if (I == 0) return MOE_OK;
-  const bool mx = desc->expert_dtype == MOE_MXFP8;
+  const bool mx = mx_act(desc);
   if (!gate || !up || !down || !gate_up_out || !down_out) return MOE_ERR_INVALID_ARG;
   if (mx && (!gate_up_scale_out || !down_scale_out)) return MOE_ERR_INVALID_ARG;
-  const int F = fmt_of(desc->expert_dtype);
+  const int F = weight_fmt(desc, shared);
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = launch_pack(gate, up, src_dtype == MOE_BF16, E, 2 * I, H, 1, F,
                                (uint8_t *)gate_up_out, (uint16_t *)gate_up_scale_out, s);
@@ -425,7 +449,7 @@ moe_status moe_grouped_ffn(moe_ctx *ctx, const moe_desc *desc, const moe_weights
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
   char *base = (char *)ws;
-  const bool mx = desc->expert_dtype == MOE_MXFP8;
+  const bool mx = mx_act(desc);
   const void *xa = x;
   const uint8_t *xs = nullptr;
   hipError_t err = hipSuccess;
@@ -485,7 +509,7 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   hipStream_t s = (hipStream_t)stream;
   char *b = (char *)ws;
   const int H = desc->hidden, E = desc->num_experts, k = desc->top_k;
-  const bool mx = desc->expert_dtype == MOE_MXFP8;
+  const bool mx = mx_act(desc);
   const bool has_shared = desc->shared_inter > 0;
   int32_t *idx = (int32_t *)(b + L.idx);
   float *tw = (float *)(b + L.w);

@@ -199,10 +199,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   const int kcn = g.K / FmtInfo<F>::chunk_elems;     // chunks along K
   const int k0 = (KSW == 4) ? wave : 0;
   const int grp_l = lane >> 4;
-  const uint8_t *wb = g.w + (size_t)e * g.w_expert_stride + (size_t)nb0 * kcn * kBlockBytes +
-                      lane * 16;
+  constexpr int WB = wblock_bytes<F>;
+  const uint8_t *wb = g.w + (size_t)e * g.w_expert_stride + (size_t)nb0 * kcn * WB + lane * 16;
   const uint16_t *wsb = nullptr;
-  if constexpr (F == FMT_MX8)
+  if constexpr (is_mx<F>)
     wsb = g.w_scale + (size_t)e * g.ws_expert_stride + (size_t)nb0 * kcn * 64 + lane;
   __shared__ f32x4 red[KSW == 4 ? 3 : 1][KSW == 4 ? NW * MB : 1][64];
 
@@ -219,7 +219,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       long long tok = token_of(g, rr);
       tp[i] = g.a + tok * g.a_row_bytes + 16 * grp_l;
       tsp[i] = nullptr;
-      if constexpr (F == FMT_MX8) tsp[i] = g.a_scale + tok * (g.K / 32) + grp_l;
+      if constexpr (is_mx<F>) tsp[i] = g.a_scale + tok * (g.K / 32) + grp_l;
     }
     f32x4 acc[NW][MB];
 #pragma unroll
@@ -228,18 +228,21 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
       for (int i = 0; i < MB; ++i) acc[n][i] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto load = [&](SkinnyBuf<F, NW, MB> &bf, int kc) MOE_INLINE {
+      // weight pieces of the chunk: four for 4 KiB blocks, two (one per
+      // half) for E2M1's 2 KiB blocks
+      constexpr int NP = WB / 1024;
 #pragma unroll
       for (int n = 0; n < NW; ++n)
 #pragma unroll
-        for (int p = 0; p < 4; ++p)
+        for (int p = 0; p < NP; ++p)
           bf.w[n][p] = __builtin_nontemporal_load(
-              (const i32x4 *)(wb + ((size_t)n * kcn + kc) * kBlockBytes + p * 1024));
+              (const i32x4 *)(wb + ((size_t)n * kcn + kc) * WB + p * 1024));
 #pragma unroll
       for (int i = 0; i < MB; ++i)
         if (i < live)
 #pragma unroll
           for (int p = 0; p < 4; ++p) bf.t[i][p] = *(const i32x4 *)(tp[i] + kc * 256 + chunk_off(0, p));
-      if constexpr (F == FMT_MX8) {
+      if constexpr (is_mx<F>) {
 #pragma unroll
         for (int n = 0; n < NW; ++n) bf.ws[n] = wsb[((size_t)n * kcn + kc) * 64];
 #pragma unroll
@@ -259,10 +262,18 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
         for (int i = 0; i < MB; ++i) {
           if (i >= live) continue;
           // MX: byte h of the scale pairs is half h's scale
-          mfma_half<F, 0, 0>(acc[n][i], bf.w[n][0], bf.w[n][1], bf.t[i][0], bf.t[i][1], bf.ws[n],
-                             bf.ts[i]);
-          mfma_half<F, 1, 1>(acc[n][i], bf.w[n][2], bf.w[n][3], bf.t[i][2], bf.t[i][3], bf.ws[n],
-                             bf.ts[i]);
+          if constexpr (F == FMT_MX4) {
+            // E2M1: piece h is all of half h's weights
+            mfma_half<F, 0, 0>(acc[n][i], bf.w[n][0], bf.w[n][0], bf.t[i][0], bf.t[i][1],
+                               bf.ws[n], bf.ts[i]);
+            mfma_half<F, 1, 1>(acc[n][i], bf.w[n][1], bf.w[n][1], bf.t[i][2], bf.t[i][3],
+                               bf.ws[n], bf.ts[i]);
+          } else {
+            mfma_half<F, 0, 0>(acc[n][i], bf.w[n][0], bf.w[n][1], bf.t[i][0], bf.t[i][1],
+                               bf.ws[n], bf.ts[i]);
+            mfma_half<F, 1, 1>(acc[n][i], bf.w[n][2], bf.w[n][3], bf.t[i][2], bf.t[i][3],
+                               bf.ws[n], bf.ts[i]);
+          }
         }
     };
 
@@ -468,13 +479,15 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
   // operands in flight.
   const __amdgpu_buffer_rsrc_t wrs = make_rsrc(g.w + (size_t)e * g.w_expert_stride,
                                               (uint32_t)g.w_expert_stride);
-  const uint32_t wvoff = (uint32_t)(nb0 * kcn) * kBlockBytes + lane * 16;
+  constexpr int TF = tok_fmt<F>;         // token-side format
+  constexpr int WB = wblock_bytes<F>;    // bytes per weight block
+  const uint32_t wvoff = (uint32_t)(nb0 * kcn) * WB + lane * 16;
   const __amdgpu_buffer_rsrc_t trs = make_rsrc(g.a, (uint32_t)g.a_bytes);
   // MX scales: weight scale pairs [row block][chunk][lane] of this expert,
   // token scale bytes [row][K / 32]
   __amdgpu_buffer_rsrc_t wsrs = wrs, tsrs = trs;
   uint32_t wsvoff = 0;
-  if constexpr (F == FMT_MX8) {
+  if constexpr (is_mx<F>) {
     wsrs = make_rsrc(g.w_scale + (size_t)e * g.ws_expert_stride,
                      (uint32_t)(g.ws_expert_stride * sizeof(uint16_t)));
     wsvoff = (uint32_t)((nb0 * kcn) * 64 + lane) * 2;
@@ -494,11 +507,11 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     tdst[i] = (rl >> 4) * 2048 + (seg >> 2) * 1024 + tslot(rl & 15, seg & 3, seg >> 2) * 16;
   }
   // MX token scales: entry idx = tid + NTH i is (token block idx / 64, lane idx % 64)
-  constexpr int TSL = (F == FMT_MX8) ? (MBT * 64 + NTH - 1) / NTH : 1;
+  constexpr int TSL = is_mx<F> ? (MBT * 64 + NTH - 1) / NTH : 1;
   uint32_t tsvoff[TSL];
 #pragma unroll
   for (int i = 0; i < TSL; ++i) tsvoff[i] = 0;
-  if constexpr (F == FMT_MX8) {
+  if constexpr (is_mx<F>) {
 #pragma unroll
     for (int i = 0; i < TSL; ++i) {
       const int idx = min(tid + NTH * i, MBT * 64 - 1);
@@ -516,7 +529,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
 #pragma unroll
     for (int i = 0; i < TLD; ++i)
       treg[i] = __builtin_amdgcn_raw_buffer_load_b128(trs, (int)tvoff[i], kc * 256 + h * 128, 0);
-    if constexpr (F == FMT_MX8) {
+    if constexpr (is_mx<F>) {
 #pragma unroll
       for (int i = 0; i < TSL; ++i)
         tsreg[i] = __builtin_amdgcn_raw_buffer_load_b8(tsrs, (int)tsvoff[i], 8 * kc + 4 * h, 0);
@@ -526,7 +539,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     uint8_t *base = tbuf(s & 1);
 #pragma unroll
     for (int i = 0; i < TLD; ++i) *(i32x4 *)(base + tdst[i]) = treg[i];
-    if constexpr (F == FMT_MX8) {
+    if constexpr (is_mx<F>) {
 #pragma unroll
       for (int i = 0; i < TSL; ++i)
         // in a partial last round the surplus threads write the last entry
@@ -544,14 +557,20 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     const int kc = s >> 1, h = s & 1;
 #pragma unroll
     for (int n = 0; n < NBW; ++n) {
-      const uint32_t so = (uint32_t)(n * kcn + kc) * kBlockBytes + h * 2048;
-      wr[set][n] = make_frag<F>(
-          __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)so, 0),
-          __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)(so + 1024), 0));
+      if constexpr (F == FMT_MX4) {
+        // E2M1: half h of the block is one 1 KiB piece
+        const uint32_t so = (uint32_t)(n * kcn + kc) * WB + h * 1024;
+        wr[set][n].v = __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)so, 0);
+      } else {
+        const uint32_t so = (uint32_t)(n * kcn + kc) * WB + h * 2048;
+        wr[set][n] = make_frag<F>(
+            __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)so, 0),
+            __builtin_amdgcn_raw_buffer_load_b128(wrs, (int)wvoff, (int)(so + 1024), 0));
+      }
       // MX: the raw scale pair of this chunk (byte h is this half's; the
       // product selects it), so nothing waits on the load before its use
       wsr[set][n] = 0;
-      if constexpr (F == FMT_MX8)
+      if constexpr (is_mx<F>)
         wsr[set][n] = __builtin_amdgcn_raw_buffer_load_b16(wsrs, (int)wsvoff,
                                                            (n * kcn + kc) * 128, 0);
     }
@@ -583,14 +602,14 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     const uint8_t *base = tbuf(slot) + wm * MBW * 2048;
     // token fragments are read one token block ahead of the products that
     // use them, so the LDS latency overlaps the matrix work
-    Frag<F> tf[2];
+    Frag<TF> tf[2];
     uint32_t tsf[2];
     auto read_frag = [&](int m, int b) MOE_INLINE {
       const uint8_t *p = base + m * 2048;
-      tf[b] = make_frag<F>(*(const i32x4 *)(p + tslot(lane & 15, lane >> 4, 0) * 16),
-                           *(const i32x4 *)(p + 1024 + tslot(lane & 15, lane >> 4, 1) * 16));
+      tf[b] = make_frag<TF>(*(const i32x4 *)(p + tslot(lane & 15, lane >> 4, 0) * 16),
+                            *(const i32x4 *)(p + 1024 + tslot(lane & 15, lane >> 4, 1) * 16));
       tsf[b] = 0;
-      if constexpr (F == FMT_MX8) tsf[b] = tscl[slot][(wm * MBW + m) * 64 + lane];
+      if constexpr (is_mx<F>) tsf[b] = tscl[slot][(wm * MBW + m) * 64 + lane];
     };
     // bf16: pin the order (the two LDS reads of block m + 1, then the eight
     // products of block m) with scheduling groups
@@ -705,7 +724,7 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     hipError_t err = launch_skinny<F, EPI, OT, HNW, MOE_HYB_MB, 1>(g, segs, stream);
     if (err != hipSuccess) return err;
   }
-  if constexpr (F == FMT_MX8) {
+  if constexpr (is_mx<F>) {
     return launch_tile<F, EPI, OT, 4, 1, MOE_TILE_TM_MX / 16, 1, MOE_TILE_OCC_MX>(g, total_rows,
                                                                                   stream);
   } else {
@@ -733,6 +752,11 @@ hipError_t launch_grouped_gemm(const GemmArgs &g, int fmt, int epi, int out_fmt,
   if (fmt == FMT_MX8) {
     if (epi == EPI_SWIGLU) return run_gemm<FMT_MX8, EPI_SWIGLU, FMT_MX8>(g, total_rows, stream);
     if (out_fmt == FMT_BF16) return run_gemm<FMT_MX8, EPI_PLAIN, FMT_BF16>(g, total_rows, stream);
+  }
+  if (fmt == FMT_MX4) {
+    // E2M1 weights, MX-fp8 tokens; the SwiGLU output is MX-fp8 like the input
+    if (epi == EPI_SWIGLU) return run_gemm<FMT_MX4, EPI_SWIGLU, FMT_MX8>(g, total_rows, stream);
+    if (out_fmt == FMT_BF16) return run_gemm<FMT_MX4, EPI_PLAIN, FMT_BF16>(g, total_rows, stream);
   }
   return hipErrorInvalidValue;
 }

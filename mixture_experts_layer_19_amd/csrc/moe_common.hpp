@@ -27,6 +27,16 @@
 // [32b, 32b + 32) of the half), so lane group g supplies the E8M0 scale of
 // MX block 4h + g while its data bytes belong to blocks g/2 and 2 + g/2.
 //
+// MXFP4 weights (W4A8).  An E2M1 chunk is 128 bytes per row, so a block of
+// 16 rows x 1 chunk is 2 KiB, stored [half][lane][16 bytes].  For E2M1 A
+// operands the scaled 16x16x128 instruction reads four registers per lane:
+// nibble i of lane group g (low nibble first) is K index 32 * g + i, and the
+// scale of K block b again comes from lane group b (measured on the device).
+// So lane group g of half h holds the contiguous MX block 4h + g of its row
+// (16 bytes), multiplies the fp8 token bytes the token layout above assigns
+// to the same K, and supplies that block's scale: the scale layout is the
+// MX-fp8 one.
+//
 // The weights are the MFMA A operand (16 output features) and the tokens
 // the B operand (16 tokens), so the 16x16 accumulator of lane l holds
 // token m = l % 16 and output features n = 4 * (l / 16) + r, r = 0..3.
@@ -48,12 +58,22 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
-enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MX8 = 2 };
+// Weight formats.  FMT_MX4 is MXFP4 (E2M1) weights multiplied with MX-fp8
+// activations; every other format uses the same type on both sides.
+enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MX8 = 2, FMT_MX4 = 3 };
 
 template <int F> struct FmtInfo;
 template <> struct FmtInfo<FMT_F32> { static constexpr int elem_bytes = 4, chunk_elems = 64; };
 template <> struct FmtInfo<FMT_BF16> { static constexpr int elem_bytes = 2, chunk_elems = 128; };
 template <> struct FmtInfo<FMT_MX8> { static constexpr int elem_bytes = 1, chunk_elems = 256; };
+template <> struct FmtInfo<FMT_MX4> { static constexpr int elem_bytes = 1, chunk_elems = 256; };
+
+// format of the token-side operand for weight format F
+template <int F> constexpr int tok_fmt = (F == FMT_MX4) ? FMT_MX8 : F;
+// block-scaled formats (E8M0 scales on both operands)
+template <int F> constexpr bool is_mx = (F == FMT_MX8 || F == FMT_MX4);
+// bytes of one packed weight block (16 rows x one K chunk)
+template <int F> constexpr int wblock_bytes = (F == FMT_MX4) ? 2048 : kBlockBytes;
 
 // ----------------------------------------------------------------------------- conversions
 
@@ -84,6 +104,30 @@ __device__ __forceinline__ uint32_t e4m3_rne(float v) {
   return sign | ((uint32_t)(e + 7) << 3) | q;
 }
 
+// OCP MX E2M1 rounding of a finite scaled value: magnitudes 0, 0.5, 1, 1.5,
+// 2, 3, 4, 6; a value between two of them goes to the nearer, a midpoint to
+// the code with mantissa bit 0 (the comparisons against the seven midpoints
+// are strict where the lower code is even), and values above 5 to 6
+// (saturation).  Sign in bit 3.
+__device__ __forceinline__ uint32_t e2m1_rne(float v) {
+  const uint32_t sign = (__float_as_uint(v) >> 28) & 0x8u;
+  const float a = fabsf(v);
+  const uint32_t c = (uint32_t)(a > 0.25f) + (uint32_t)(a >= 0.75f) + (uint32_t)(a > 1.25f) +
+                     (uint32_t)(a >= 1.75f) + (uint32_t)(a > 2.5f) + (uint32_t)(a >= 3.5f) +
+                     (uint32_t)(a > 5.0f);
+  return sign | c;
+}
+
+// Shared exponent of an MXFP4 block: X = floor(log2 amax) - 2 (2 is the
+// exponent of E2M1's largest normal, 6), clamped below at -127.  Returned
+// as the E8M0 byte X + 127.
+__device__ __forceinline__ uint32_t mx4_scale_byte(float amax) {
+  int ef = (int)((__float_as_uint(amax) >> 23) & 0xFFu);
+  int X = ef - 127 - 2;
+  if (ef == 0 || X < -127) X = -127;
+  return (uint32_t)(X + 127);
+}
+
 // Shared exponent X of an MX block from its largest magnitude (exact):
 // X = floor(log2 amax) - 8, clamped below at -127 (zero and fp32-subnormal
 // maxima give -127).  Returned as the E8M0 byte X + 127.
@@ -94,7 +138,7 @@ __device__ __forceinline__ uint32_t mx_scale_byte(float amax) {
   return (uint32_t)(X + 127);
 }
 
-// 2^-X as an fp32 for an E8M0 byte s = X + 127 (X in [-127, 119]).
+// 2^-X as an fp32 for an E8M0 byte s = X + 127 (X in [-127, 125]).
 __device__ __forceinline__ float mx_inv_scale(uint32_t s) {
   return __uint_as_float((uint32_t)(254 - (int)s) << 23);
 }
@@ -168,6 +212,14 @@ __device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32
     for (int e = 0; e < 4; ++e)
       acc = __builtin_amdgcn_mfma_f32_16x16x4f32(__int_as_float(w1[e]), __int_as_float(t1[e]), acc,
                                                  0, 0, 0);
+  } else if constexpr (F == FMT_MX4) {
+    // A: the half's E2M1 piece (w0; only four registers are read for E2M1),
+    // operand format 4 = E2M1; B: fp8 E4M3 tokens
+    const i32x4 z = {0, 0, 0, 0};
+    const i32x8 a = __builtin_shufflevector(w0, z, 0, 1, 2, 3, 4, 5, 6, 7);
+    const i32x8 b = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, WSEL, (int)ws, TSEL,
+                                                           (int)ts);
   } else {
     const i32x8 a = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
     const i32x8 b = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -188,12 +240,19 @@ template <>
 struct Frag<FMT_MX8> {
   i32x8 v;
 };
+// E2M1 weights: one 16-byte piece per half-chunk
+template <>
+struct Frag<FMT_MX4> {
+  i32x4 v;
+};
 
 template <int F>
 __device__ __forceinline__ Frag<F> make_frag(const i32x4 &a, const i32x4 &b) {
   Frag<F> f;
   if constexpr (F == FMT_MX8) {
     f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
+  } else if constexpr (F == FMT_MX4) {
+    f.v = a;
   } else {
     f.p0 = a;
     f.p1 = b;
@@ -201,11 +260,18 @@ __device__ __forceinline__ Frag<F> make_frag(const i32x4 &a, const i32x4 &b) {
   return f;
 }
 
+// acc += W x T over one half-chunk from a weight fragment (format F) and a
+// token fragment (format tok_fmt<F>).
 template <int F, int WSEL = 0>
-__device__ __forceinline__ void mfma_frag(f32x4 &acc, const Frag<F> &w, const Frag<F> &t,
+__device__ __forceinline__ void mfma_frag(f32x4 &acc, const Frag<F> &w, const Frag<tok_fmt<F>> &t,
                                           uint32_t ws, uint32_t ts) {
   if constexpr (F == FMT_MX8) {
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.v, t.v, acc, 0, 0, WSEL, (int)ws, 0,
+                                                           (int)ts);
+  } else if constexpr (F == FMT_MX4) {
+    const i32x4 z = {0, 0, 0, 0};
+    const i32x8 a = __builtin_shufflevector(w.v, z, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, t.v, acc, 4, 0, WSEL, (int)ws, 0,
                                                            (int)ts);
   } else {
     mfma_half<F>(acc, w.p0, w.p1, t.p0, t.p1, ws, ts);

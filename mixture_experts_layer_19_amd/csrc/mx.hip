@@ -9,7 +9,9 @@
 // activations quantised on the fly.
 //
 // Weight packing produces the 4 KiB fragment blocks described in
-// moe_common.hpp, ordered [expert][16-row block][256-byte K chunk].  For the
+// moe_common.hpp, ordered [expert][16-row block][256-byte K chunk] (2 KiB
+// blocks of 256 K elements for MXFP4, whose E2M1 elements follow the same
+// OCP specification with X = floor(log2 max|v|) - 2).  For the
 // gate/up matrix the row blocks alternate: block 2j holds gate rows
 // 16j..16j+15 and block 2j+1 the up rows with the same indices, so the SwiGLU
 // epilogue finds a gate value and its up value in the same lane.
@@ -36,6 +38,24 @@ __device__ __forceinline__ void mx_block(const float (&v)[32], uint32_t (&codes)
     uint32_t c = 0;
 #pragma unroll
     for (int b = 0; b < 4; ++b) c |= e4m3_rne(v[4 * w + b] * inv) << (8 * b);
+    codes[w] = c;
+  }
+}
+
+// Quantise 32 values to MXFP4: E2M1 codes (nibble i of word i / 8, low
+// nibble first) and the scale byte.
+__device__ __forceinline__ void mx4_block(const float (&v)[32], uint32_t (&codes)[4],
+                                          uint32_t &sb) {
+  float am = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) am = fmaxf(am, fabsf(v[i]));
+  sb = mx4_scale_byte(am);
+  const float inv = mx_inv_scale(sb);
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) c |= e2m1_rne(v[8 * w + j] * inv) << (4 * j);
     codes[w] = c;
   }
 }
@@ -108,8 +128,26 @@ __global__ __launch_bounds__(256) void pack_kernel(const void *__restrict__ a,
     row = v;
   }
   const long long base = ((long long)e * src_rows + row) * K + (long long)kc * CE;
-  uint8_t *blk = out + (((long long)e * nbtot + nb) * kcn + kc) * kBlockBytes;
-  if constexpr (F == FMT_MX8) {
+  uint8_t *blk = out + (((long long)e * nbtot + nb) * kcn + kc) * wblock_bytes<F>;
+  if constexpr (F == FMT_MX4) {
+    // E2M1: lane group g of half h holds MX block 4h + g of the row (16
+    // bytes, contiguous K) and supplies its scale, like the MX-fp8 layout
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      uint32_t sc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float vals[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) vals[i] = load_src<BF16>(src, base + 32 * (4 * h + g) + i);
+        uint32_t c[4];
+        mx4_block(vals, c, sc[h]);
+        *(uint4 *)(blk + h * 1024 + (r16 + 16 * g) * 16) = make_uint4(c[0], c[1], c[2], c[3]);
+      }
+      scale_out[(((long long)e * nbtot + nb) * kcn + kc) * 64 + r16 + 16 * g] =
+          (uint16_t)(sc[0] | (sc[1] << 8));
+    }
+  } else if constexpr (F == FMT_MX8) {
     uint32_t sc[8];
     uint32_t codes[8][8];
 #pragma unroll
@@ -157,6 +195,7 @@ hipError_t launch_pack(const void *a, const void *b, int src_is_bf16, int E, int
                        int gate_up, int fmt, uint8_t *out, uint16_t *scale_out,
                        hipStream_t stream) {
   int ce = fmt == FMT_F32 ? 64 : (fmt == FMT_BF16 ? 128 : 256);
+  if (fmt < FMT_F32 || fmt > FMT_MX4) return hipErrorInvalidValue;
   const long long total = (long long)E * N * (K / ce);
   if (total <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((total + 255) / 256);
@@ -165,11 +204,13 @@ hipError_t launch_pack(const void *a, const void *b, int src_is_bf16, int E, int
   if (src_is_bf16) {
     if (fmt == FMT_F32) MOE_PACK(true, FMT_F32);
     else if (fmt == FMT_BF16) MOE_PACK(true, FMT_BF16);
-    else MOE_PACK(true, FMT_MX8);
+    else if (fmt == FMT_MX8) MOE_PACK(true, FMT_MX8);
+    else MOE_PACK(true, FMT_MX4);
   } else {
     if (fmt == FMT_F32) MOE_PACK(false, FMT_F32);
     else if (fmt == FMT_BF16) MOE_PACK(false, FMT_BF16);
-    else MOE_PACK(false, FMT_MX8);
+    else if (fmt == FMT_MX8) MOE_PACK(false, FMT_MX8);
+    else MOE_PACK(false, FMT_MX4);
   }
 #undef MOE_PACK
   return hipGetLastError();

@@ -13,6 +13,8 @@ and the Hy4-preview tutorial, section 1):
   hy3_prefill  T=8192, H=4096, E=192, k=8, I=Is=1536, bf16
   hy4_skew     T=2048, H=4096, E=256, k=8, I=Is=1536, bf16, Zipf logit bias
   mx           T=4096, H=4096, E=192, k=8, I=Is=1536, MX-fp8 experts
+  w4a8_decode  T=64,   H=4096, E=192, k=8, I=Is=1536, MXFP4 routed experts (W4A8)
+  w4a8         T=4096, H=4096, E=192, k=8, I=Is=1536, MXFP4 routed experts (W4A8)
 
 Distributions: activations N(0,1); router and expert weights N(0, 0.02);
 router weights stay fp32.  Every tensor has its own PCG64 stream derived from
@@ -47,7 +49,8 @@ class Workload:
     k: int
     I: int
     Is: int
-    dtype: str                 # "f32", "bf16" or "mxfp8" (expert weights + activations)
+    dtype: str                 # "f32", "bf16", "mxfp8" (expert weights + activations) or
+                               # "w4a8" (MXFP4 routed experts, MX-fp8 shared and activations)
     rho: float = ROUTER_SCALING_FACTOR
     route_norm: bool = True
     zipf_beta: float = 0.0     # 0: no router bias
@@ -68,6 +71,9 @@ WORKLOADS = {
     "hy4_skew": Workload("hy4_skew", T=2048, H=4096, E=256, k=8, I=1536, Is=1536, dtype="bf16",
                          zipf_beta=0.38),
     "mx": Workload("mx", T=4096, H=4096, E=192, k=8, I=1536, Is=1536, dtype="mxfp8"),
+    "w4a8_decode": Workload("w4a8_decode", T=64, H=4096, E=192, k=8, I=1536, Is=1536,
+                            dtype="w4a8"),
+    "w4a8": Workload("w4a8", T=4096, H=4096, E=192, k=8, I=1536, Is=1536, dtype="w4a8"),
 }
 
 

@@ -15,7 +15,9 @@ from . import inputs as I
 
 _DT = {"f32": (B.MOE_F32, B.MOE_F32, B.MOE_F32),
        "bf16": (B.MOE_BF16, B.MOE_BF16, B.MOE_BF16),
-       "mxfp8": (B.MOE_BF16, B.MOE_MXFP8, B.MOE_BF16)}
+       "mxfp8": (B.MOE_BF16, B.MOE_MXFP8, B.MOE_BF16),
+       # W4A8: MXFP4 routed experts, MX-fp8 shared expert and activations
+       "w4a8": (B.MOE_BF16, B.MOE_MXFP4, B.MOE_BF16)}
 
 
 def desc_for(w: I.Workload) -> B.MoeDesc:
@@ -50,7 +52,7 @@ class DeviceLayer:
         nb = lambda shared, which: B.moe_packed_bytes(d, shared, which)
         self.gate_up = torch.empty(nb(0, B.MOE_PACK_GATE_UP), dtype=u8, device=self.dev)
         self.down = torch.empty(nb(0, B.MOE_PACK_DOWN), dtype=u8, device=self.dev)
-        mx = w.dtype == "mxfp8"
+        mx = w.dtype in ("mxfp8", "w4a8")
         self.gate_up_s = torch.empty(nb(0, B.MOE_PACK_GATE_UP_SCALE), dtype=u8, device=self.dev) if mx else None
         self.down_s = torch.empty(nb(0, B.MOE_PACK_DOWN_SCALE), dtype=u8, device=self.dev) if mx else None
         self.sh_gate_up = torch.empty(nb(1, B.MOE_PACK_GATE_UP), dtype=u8, device=self.dev)

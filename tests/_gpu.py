@@ -9,9 +9,16 @@ import numpy as np
 from mixture_experts_layer_19_amd import inputs as I
 
 TIE_MARGIN = 1e-6          # sigmoid-score margin inside which a routing flip is a tie
-TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 3e-2}
+TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 3e-2, "w4a8": 3e-2}
 
 _layers = {}
+
+
+def oracle_mx(dtype: str, shared: bool = False) -> int:
+    """Oracle MX mode for a workload dtype: 0 none, 1 MX-fp8, 2 W4A8 (whose
+    shared expert is MX-fp8)."""
+    m = {"mxfp8": 1, "w4a8": 2}.get(dtype, 0)
+    return 1 if (shared and m == 2) else m
 
 
 def device_layer(w: I.Workload):
@@ -81,6 +88,18 @@ def unpack_scales(packed: np.ndarray, E: int, N: int, K: int) -> np.ndarray:
     b = packed.view(np.uint8).reshape(E, nb, kc, 4, 16, 2)   # e nb kc g r h
     b = b.transpose(0, 1, 4, 2, 5, 3)                         # e nb r kc h g
     return b.reshape(E, N, K // 32)
+
+
+def unpack_blocks_e2m1(packed: np.ndarray, E: int, N: int, K: int) -> np.ndarray:
+    """Inverse of the MXFP4 packed layout: bytes [E, N/16, K/256, half 2,
+    lane group 4, row 16, 16 bytes] -> E2M1 codes [E, N, K] (one per byte),
+    where lane group g of half h holds K [128 h + 32 g, +32) of its row, two
+    codes per byte, low nibble first."""
+    nb, kc = N // 16, K // 256
+    a = packed.reshape(E, nb, kc, 2, 4, 16, 16)               # e nb kc h g r byte
+    codes = np.stack([a & 15, a >> 4], axis=-1).reshape(E, nb, kc, 2, 4, 16, 32)
+    codes = codes.transpose(0, 1, 5, 2, 3, 4, 6)              # e nb r kc h g i
+    return codes.reshape(E, N, K)
 
 
 def virtual_to_gate_up(dense: np.ndarray, I_: int):

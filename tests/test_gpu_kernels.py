@@ -11,8 +11,8 @@ from mixture_experts_layer_19_amd import binding as B
 from mixture_experts_layer_19_amd import inputs as I
 from mixture_experts_layer_19_amd.layer import desc_for, to_device
 
-from _gpu import (TOL, classify_routing, rel_max_err, to_numpy, unpack_blocks, unpack_scales,
-                  virtual_to_gate_up)
+from _gpu import (TOL, classify_routing, oracle_mx, rel_max_err, to_numpy, unpack_blocks,
+                  unpack_blocks_e2m1, unpack_scales, virtual_to_gate_up)
 
 pytestmark = pytest.mark.gpu
 
@@ -56,6 +56,44 @@ def test_mx_quantize_bit_exact(orc, src):
     oq, os_ = orc.mxq(ref)
     np.testing.assert_array_equal(s.cpu().numpy(), os_)
     np.testing.assert_array_equal(q.cpu().numpy(), oq)
+
+
+def test_pack_experts_w4a8_layout(orc):
+    """MXFP4 routed experts: E2M1 codes and E8M0 scales bit-exact against the
+    oracle's MXFP4 rule; the shared expert of the same layer packs as MX-fp8."""
+    w = I.Workload("pack4", T=1, H=512, E=3, k=2, I=256, Is=256, dtype="w4a8")
+    d = desc_for(w)
+    masters = [I.expert_master(w, e) for e in range(w.E)]
+    src = [np.stack([m[i] for m in masters]) for i in range(3)]
+    nb = lambda sh, which: B.moe_packed_bytes(d, sh, which)
+    assert nb(0, B.MOE_PACK_GATE_UP) == w.E * 2 * w.I * w.H // 2
+    assert nb(0, B.MOE_PACK_GATE_UP_SCALE) == w.E * 2 * w.I * w.H // 32
+    assert nb(1, B.MOE_PACK_GATE_UP) == 2 * w.Is * w.H
+    u8 = lambda n: torch.empty(n, dtype=torch.uint8, device="cuda")
+    gu, dn = u8(nb(0, B.MOE_PACK_GATE_UP)), u8(nb(0, B.MOE_PACK_DOWN))
+    gus, dns = u8(nb(0, B.MOE_PACK_GATE_UP_SCALE)), u8(nb(0, B.MOE_PACK_DOWN_SCALE))
+    B.moe_pack_experts(d, 0, B.MOE_F32, dev(src[0]), dev(src[1]), dev(src[2]), gu, dn, gus, dns)
+    sh = I.shared_master(w)
+    sgu, sdn = u8(nb(1, B.MOE_PACK_GATE_UP)), u8(nb(1, B.MOE_PACK_DOWN))
+    sgus, sdns = u8(nb(1, B.MOE_PACK_GATE_UP_SCALE)), u8(nb(1, B.MOE_PACK_DOWN_SCALE))
+    B.moe_pack_experts(d, 1, B.MOE_F32, dev(sh[0][None]), dev(sh[1][None]), dev(sh[2][None]),
+                       sgu, sdn, sgus, sdns)
+    torch.cuda.synchronize()
+    g_c, u_c = virtual_to_gate_up(unpack_blocks_e2m1(gu.cpu().numpy(), w.E, 2 * w.I, w.H), w.I)
+    d_c = unpack_blocks_e2m1(dn.cpu().numpy(), w.E, w.H, w.I)
+    sg, su = virtual_to_gate_up(unpack_scales(gus.cpu().numpy().view(np.uint16), w.E, 2 * w.I, w.H), w.I)
+    sd = unpack_scales(dns.cpu().numpy().view(np.uint16), w.E, w.H, w.I)
+    for arr, sc, ref in ((g_c, sg, src[0]), (u_c, su, src[1]), (d_c, sd, src[2])):
+        oq, os_ = orc.mxq4(ref)
+        np.testing.assert_array_equal(sc, os_)
+        np.testing.assert_array_equal(arr, oq)
+    # shared expert: MX-fp8 bytes
+    sg_b, su_b = virtual_to_gate_up(unpack_blocks(sgu.cpu().numpy(), 1, 2 * w.Is, w.H), w.Is)
+    ssg, ssu = virtual_to_gate_up(unpack_scales(sgus.cpu().numpy().view(np.uint16), 1, 2 * w.Is, w.H), w.Is)
+    for arr, sc, ref in ((sg_b, ssg, sh[0][None]), (su_b, ssu, sh[1][None])):
+        oq, os_ = orc.mxq(ref)
+        np.testing.assert_array_equal(sc, os_)
+        np.testing.assert_array_equal(arr, oq)
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "mxfp8", "f32"])
@@ -300,7 +338,7 @@ def _ffn_case(orc, ctx, w, T, tag, shared=False, idx=None):
                           None if shared else dev(src), None if shared else dev(offs), yt, ws, n)
         torch.cuda.synchronize()
         y = to_numpy(yt)
-        mx = w.dtype == "mxfp8"
+        mx = oracle_mx(w.dtype, shared)
         if shared:
             _, ref = orc.swiglu_rows(x, *I.shared_stored(w), mx=mx)
         else:
@@ -329,6 +367,9 @@ def _ffn_case(orc, ctx, w, T, tag, shared=False, idx=None):
     ("mxfp8", 1024, 1536, 12, 4, 30),   # streaming, MX
     ("mxfp8", 1024, 1536, 3, 2, 400),   # tiled, MX
     ("mxfp8", 1024, 1536, 12, 2, 300),  # mixed, MX
+    ("w4a8", 1024, 1536, 12, 4, 30),    # streaming, MXFP4 weights x MX-fp8 tokens
+    ("w4a8", 1024, 1536, 3, 2, 400),    # tiled, W4A8
+    ("w4a8", 1024, 1536, 12, 2, 300),   # mixed, W4A8
 ])
 def test_grouped_ffn_parity(orc, ctx, dtype, H, I_, E, k, T):
     w = I.Workload("ffn", T=T, H=H, E=E, k=k, I=I_, Is=I_, dtype=dtype)
@@ -338,10 +379,11 @@ def test_grouped_ffn_parity(orc, ctx, dtype, H, I_, E, k, T):
 
 
 @pytest.mark.parametrize("dtype,T", [("f32", 50), ("f32", 200), ("bf16", 64), ("bf16", 333),
-                                     ("mxfp8", 20), ("mxfp8", 333)])
+                                     ("mxfp8", 20), ("mxfp8", 333), ("w4a8", 20)])
 def test_shared_ffn_parity(orc, ctx, dtype, T):
-    Iw = 1536 if dtype == "mxfp8" else 256
-    H = 1024 if dtype == "mxfp8" else 512
+    # (the shared expert of a W4A8 layer is MX-fp8)
+    Iw = 1536 if dtype in ("mxfp8", "w4a8") else 256
+    H = 1024 if dtype in ("mxfp8", "w4a8") else 512
     w = I.Workload("shared", T=T, H=H, E=4, k=2, I=Iw, Is=Iw, dtype=dtype)
     err = _ffn_case(orc, ctx, w, T, tag=2, shared=True)
     print("[shared ffn] %s T=%d rel err %.3g" % (dtype, T, err))

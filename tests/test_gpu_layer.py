@@ -1,6 +1,6 @@
 """Whole-layer parity: moe_layer_forward (routing, permutation, grouped FFN,
 shared expert on the side stream, combine) against the oracle on the five
-workloads.  The tiny workload is compared on every output; the full-size
+workloads and the W4A8 (MXFP4 routed experts) ones.  The tiny workload is compared on every output; the full-size
 workloads on sampled tokens the oracle evaluates one by one from the
 definition, in the same launch configuration the benchmark times.  Tokens
 whose routing differs from the oracle's only by ties within 1e-6 of the
@@ -15,8 +15,8 @@ from mixture_experts_layer_19_amd import binding as B
 from mixture_experts_layer_19_amd import inputs as I
 from mixture_experts_layer_19_amd.layer import DeviceLayer, to_device
 
-from _gpu import (TOL, classify_routing, device_layer, expert_weights_parallel, rel_max_err,
-                  to_numpy)
+from _gpu import (TOL, classify_routing, device_layer, expert_weights_parallel, oracle_mx,
+                  rel_max_err, to_numpy)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def _check_layer(orc, name, T=None, full=False, w=None):
     ew = expert_weights_parallel(w, experts)
     ref, o_idx, _, _ = orc.layer_forward_tokens(
         keep, x, Wr, b, lambda e: ew[e], I.shared_stored(w), k=w.k, rho=w.rho,
-        route_norm=w.route_norm, mx=(w.dtype == "mxfp8"))
+        route_norm=w.route_norm, mx=oracle_mx(w.dtype))
     np.testing.assert_array_equal(o_idx, o_idx_all[keep])
     err = rel_max_err(out[keep], ref)
     print("[layer] %s T=%d: %d tokens compared, %d tie flips, rel err %.3g"
@@ -92,18 +92,28 @@ def test_layer_mx_sampled(orc):
     _check_layer(orc, "mx")
 
 
+def test_layer_w4a8_decode_all_tokens(orc):
+    # MXFP4 routed experts, MX-fp8 shared expert and activations
+    _check_layer(orc, "w4a8_decode", full=True)
+
+
+def test_layer_w4a8_sampled(orc):
+    _check_layer(orc, "w4a8")
+
+
 @pytest.mark.parametrize("T", [1, 5, 77, 300])
 def test_layer_ragged_token_counts(orc, T):
     _check_layer(orc, "hy3_decode", T=T, full=T <= 77)
 
 
 @pytest.mark.parametrize("dtype,E,k,T", [("bf16", 1024, 16, 300), ("f32", 1024, 16, 70),
-                                         ("bf16", 1024, 1, 260), ("mxfp8", 1024, 16, 40)])
+                                         ("bf16", 1024, 1, 260), ("mxfp8", 1024, 16, 40),
+                                         ("w4a8", 1024, 16, 40)])
 def test_layer_largest_expert_count_and_top_k(orc, dtype, E, k, T):
     # the largest E and k the library accepts (1024, 16), and k = 1, on a
     # narrow layer so the oracle stays quick; every token is compared.  MX
     # needs hidden and intermediate sizes in whole 256-element chunks.
-    H, Iw = (512, 256) if dtype == "mxfp8" else (256, 128)
+    H, Iw = (512, 256) if dtype in ("mxfp8", "w4a8") else (256, 128)
     w = I.Workload("maxes", T=T, H=H, E=E, k=k, I=Iw, Is=Iw, dtype=dtype)
     _check_layer(orc, "maxes", w=w, full=True)
 
