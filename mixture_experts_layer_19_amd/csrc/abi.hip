@@ -18,10 +18,16 @@
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
 
+// Batches of at most this many tokens start the shared expert on the side
+// stream before gating; larger ones start it beside the routed down GEMM.
+#ifndef MOE_SHARED_EARLY_T
+#define MOE_SHARED_EARLY_T 64
+#endif
+
 struct moe_ctx {
   int device;
   hipStream_t side;
-  hipEvent_t ev_ready;   // recorded on the caller's stream once the routed gate/up is queued
+  hipEvent_t ev_ready;   // recorded on the caller's stream where the shared expert may start
   hipEvent_t ev_done;    // recorded on the side stream after the shared expert
   char last_error[256];
   int profiling;
@@ -536,12 +542,18 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
     xa = b + L.xq;
     xs = (const uint8_t *)b + L.xs;
   }
-  // Shared expert on the side stream.  It needs only the activations; it is
-  // started once the routed gate/up GEMM is queued (the input-ready event is
-  // recorded after it), so it runs beside the routed down GEMM: beside gating
-  // and permutation it slows those short, latency-bound kernels by more than
-  // it saves.
+  // Shared expert on the side stream.  It needs only the activations.  For
+  // larger batches it is started once the routed gate/up GEMM is queued (the
+  // input-ready event is recorded after it), so it runs beside the routed
+  // down GEMM: beside gating and permutation it slows those short,
+  // latency-bound kernels by more than it saves.  For decode-sized batches
+  // (T <= MOE_SHARED_EARLY_T) with MX experts it starts at once, beside
+  // gating and the routed gate/up GEMM: there the routed down GEMM (4- or
+  // 8-bit weights) is shorter than the MX-fp8 shared expert, which would
+  // otherwise lengthen the layer (W4A8 decode 0.398 -> 0.370 ms).  A bf16
+  // decode batch keeps the late start (the early one slows gating, +0.4%).
   const bool two = has_shared && ctx->side && ctx->side != s;
+  const bool early = two && mx && T <= MOE_SHARED_EARLY_T;
   auto shared_expert = [&]() -> hipError_t {
     hipStream_t ss = two ? ctx->side : s;
     hipError_t e;
@@ -551,6 +563,10 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
     if (e != hipSuccess) return e;
     return two ? hipEventRecord(ctx->ev_done, ss) : hipSuccess;
   };
+  if (early) {
+    MOE_TRY(hipEventRecord(ctx->ev_ready, s), "input-ready event");
+    MOE_TRY(shared_expert(), "shared expert");
+  }
   // Gating on the main stream.
   MOE_TRY(tm.start(MOE_STAGE_ROUTE, s), "timing");
   MOE_TRY(launch_route(x, desc->act_dtype == MOE_BF16, w->router_w, w->router_bias,
@@ -565,9 +581,10 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
           "permutation");
   MOE_TRY(tm.stop(MOE_STAGE_PERMUTE, s), "timing");
   MOE_TRY(ffn(desc, w, 0, xa, xs, T, src, offsets, b + L.y, b + L.h,
-              mx ? (uint8_t *)b + L.hs : nullptr, s, &tm, two ? ctx->ev_ready : nullptr),
+              mx ? (uint8_t *)b + L.hs : nullptr, s, &tm,
+              two && !early ? ctx->ev_ready : nullptr),
           "routed experts");
-  if (has_shared) MOE_TRY(shared_expert(), "shared expert");
+  if (has_shared && !early) MOE_TRY(shared_expert(), "shared expert");
   // Join, then FinalizeRouting + shared add.
   if (two) MOE_TRY(hipStreamWaitEvent(s, ctx->ev_done, 0), "main stream wait");
   const int of = fmt_of(desc->out_dtype);
