@@ -70,6 +70,11 @@ def _load():
         lib.oracle_e2m1_encode.restype = ctypes.c_uint8
         lib.oracle_e2m1_encode.argtypes = [ctypes.c_double]
         lib.oracle_mxq4.argtypes = [I64, P, P, P]
+        lib.oracle_fp8_tensor_scale.restype = ctypes.c_float
+        lib.oracle_fp8_tensor_scale.argtypes = [I64, P]
+        lib.oracle_fp8_quantize.argtypes = [I64, P, ctypes.c_float, P]
+        lib.oracle_swiglu_rows_fp8.argtypes = [I64, I64, I64, P, P, P, P, ctypes.c_float,
+                                               ctypes.c_float, P, P]
         lib.oracle_mx4_dequant.argtypes = [I64, P, P, P]
         lib.oracle_router_logits.argtypes = [I64, I64, I64, P, P, P, P]
         lib.oracle_route.argtypes = [I64, I64, I64, I64, P, P, P, ctypes.c_float, ctypes.c_int,
@@ -82,6 +87,7 @@ def _load():
             [I64, I64, I64, I64, I64, I64, ctypes.c_float, ctypes.c_int, P, P, P, ctypes.c_int]
             + [P] * 6 + [ctypes.c_int] + [P] * 10)
         for name in ("oracle_mxq", "oracle_mx_dequant", "oracle_mxq4", "oracle_mx4_dequant",
+                     "oracle_fp8_quantize", "oracle_swiglu_rows_fp8",
                      "oracle_router_logits", "oracle_route",
                      "oracle_permute", "oracle_swiglu_rows", "oracle_combine",
                      "oracle_layer_forward"):
@@ -186,6 +192,39 @@ def mx4_dequant(q, s):
     v = np.empty(q.shape, np.float32)
     _check(_load().oracle_mx4_dequant(q.size // 32, _p(q), _p(s), _p(v)), "mx4_dequant")
     return v
+
+
+# ----------------------------------------------------------------------------- static FP8
+
+
+def fp8_tensor_scale(w) -> float:
+    """Per-tensor weight scale fp32(max|w| / 448) (1 for an all-zero tensor)."""
+    w = _f32(w)
+    return float(_load().oracle_fp8_tensor_scale(w.size, _p(w)))
+
+
+def fp8_quantize(v, s):
+    """E4M3 codes of fp32(v / s) (round to nearest even, saturating)."""
+    v = _f32(v)
+    q = np.empty(v.shape, np.uint8)
+    _check(_load().oracle_fp8_quantize(v.size, _p(v), ctypes.c_float(s), _p(q)), "fp8_quantize")
+    return q
+
+
+def swiglu_rows_fp8(xrows, Wg, Wu, Wd, s_x, s_h):
+    """One expert's SwiGLU FFN with static per-tensor FP8 (fp32 masters in;
+    weight scales from fp8_tensor_scale, activation scales s_x and s_h).
+    Returns (h [M,I] before quantisation, y [M,H])."""
+    xrows = _f32(xrows)
+    M, H = xrows.shape
+    Wg, Wu, Wd = _f32(Wg), _f32(Wu), _f32(Wd)
+    I = Wg.shape[0]
+    h = np.empty((M, I), np.float32)
+    y = np.empty((M, H), np.float32)
+    _check(_load().oracle_swiglu_rows_fp8(M, H, I, _p(xrows), _p(Wg), _p(Wu), _p(Wd),
+                                          ctypes.c_float(s_x), ctypes.c_float(s_h), _p(h), _p(y)),
+           "swiglu_rows_fp8")
+    return h, y
 
 
 def _mx_mode(mx) -> int:
@@ -303,11 +342,13 @@ def layer_forward(x, Wr, bias, Wg, Wu, Wd, Sg=None, Su=None, Sd=None, *, k, rho,
 
 
 def layer_forward_tokens(tokens, x, Wr, bias, expert_weights, shared_weights, *, k, rho,
-                         route_norm=True, mx=False):
+                         route_norm=True, mx=False, fp8=None):
     """Layer output for selected tokens only, straight from the definition.
 
     ``expert_weights(e)`` returns (Wg [I,H], Wu [I,H], Wd [H,I]) of expert e;
-    ``shared_weights`` is (Sg, Su, Sd) or None.  Returns (out [n,H],
+    ``shared_weights`` is (Sg, Su, Sd) or None.  ``fp8`` = (s_x, s_h, s_h_shared)
+    selects static per-tensor FP8 experts (fp32 masters in, quantised here)
+    with those activation scales; otherwise ``mx`` applies.  Returns (out [n,H],
     topk_idx [n,k], topk_w [n,k], gap [n]) for ``x[tokens]``."""
     tokens = np.asarray(tokens, dtype=np.int64)
     xs = _f32(np.asarray(x)[tokens])
@@ -323,11 +364,16 @@ def layer_forward_tokens(tokens, x, Wr, bias, expert_weights, shared_weights, *,
     for e, lst in sorted(rows_of.items()):
         Wg, Wu, Wd = expert_weights(e)
         rows = np.array([i for i, _ in lst])
-        _, y = swiglu_rows(xs[rows], Wg, Wu, Wd, mx=mx)
+        if fp8 is not None:
+            _, y = swiglu_rows_fp8(xs[rows], Wg, Wu, Wd, fp8[0], fp8[1])
+        else:
+            _, y = swiglu_rows(xs[rows], Wg, Wu, Wd, mx=mx)
         for (i, j), yr in zip(lst, y):
             yk[i, j] = yr
     zsh = None
-    if shared_weights is not None:
+    if shared_weights is not None and fp8 is not None:
+        _, zsh = swiglu_rows_fp8(xs, *shared_weights, fp8[0], fp8[2])
+    elif shared_weights is not None:
         # the shared expert of a W4A8 layer stays W8A8
         _, zsh = swiglu_rows(xs, *shared_weights, mx=MX_FP8 if _mx_mode(mx) == MX_W4A8 else mx)
     # Rows of yk are already in (token, slot) order, so dest is the identity.

@@ -20,6 +20,9 @@
  *     [out, in] (a reading: the pages give only the sizes).
  *   - MX-fp8: OCP Microscaling Formats (MX) v1.0 specification, 32-element
  *     blocks, E8M0 shared scale, E4M3 (FN variant) elements.
+ *   - Static per-tensor FP8 W8A8 (the FP8 checkpoints of the Hy3 guide,
+ *     section 2, and the Hy4 tutorial's w8a8 weights): one scale per weight
+ *     tensor, max|w| / 448, and fixed activation scales.
  *   - MXFP4 (W4A8 routed experts, Hy3 guide section 8.2): the same
  *     specification's E2M1 elements with the same 32-element E8M0 blocks;
  *     activations stay MX-fp8 and the shared expert stays W8A8.
@@ -455,6 +458,100 @@ ORC_EXPORT int oracle_swiglu_rows(int64_t M, int64_t H, int64_t I, const float *
   free(wg_q);
   free(wu_q);
   free(wd_q);
+  return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Static per-tensor FP8 (W8A8 with one scale per tensor)               */
+/* ------------------------------------------------------------------ */
+
+/* Per-tensor scale of a weight matrix: s = fp32(max|w| / 448), so the
+ * largest element maps to E4M3's largest normal; an all-zero tensor takes
+ * s = 1.  (FP8 checkpoints of the Hy3 and Hy4 families carry one such scale
+ * per weight tensor; the pages name the format only.) */
+ORC_EXPORT float oracle_fp8_tensor_scale(int64_t n, const float *w) {
+  float amax = 0.0f;
+  for (int64_t i = 0; i < n; ++i) {
+    float a = fabsf(w[i]);
+    if (a > amax) amax = a;
+  }
+  return amax == 0.0f ? 1.0f : amax / 448.0f;
+}
+
+/* E4M3 codes of v under a per-tensor scale s: code = E4M3(fp32(v / s)),
+ * round to nearest even, saturating. */
+ORC_EXPORT int oracle_fp8_quantize(int64_t n, const float *v, float s, uint8_t *q) {
+  if (n < 0 || (n > 0 && (!v || !q)) || !(s > 0.0f)) return -1;
+  for (int64_t i = 0; i < n; ++i) {
+    float scaled = v[i] / s;
+    q[i] = oracle_e4m3_encode((double)scaled);
+  }
+  return 0;
+}
+
+/* Dequantised values E4M3(q) * s, in double (exact: at most 4 + 24
+ * significant bits). */
+static void fp8_dequant_d(int64_t n, const float *v, float s, double *out) {
+  for (int64_t i = 0; i < n; ++i) {
+    float scaled = v[i] / s;
+    out[i] = oracle_e4m3_decode(oracle_e4m3_encode((double)scaled)) * (double)s;
+  }
+}
+
+/* One expert's SwiGLU FFN with static per-tensor FP8: each weight matrix
+ * (fp32 masters Wg [I,H], Wu [I,H], Wd [H,I]) quantised with its own
+ * oracle_fp8_tensor_scale, the rows x [M,H] with the static activation
+ * scale s_x, and h with the static scale s_h:
+ *   g_i = sum_h x~_h Wg~[i,h],  u_i = sum_h x~_h Wu~[i,h]      (double)
+ *   h_i = fp32( silu(g_i) * u_i )
+ *   y_n = fp32( sum_i h~_i Wd~[n,i] )
+ * where a~ is the dequantised E4M3 value of a.  h_out [M,I] (optional)
+ * receives h before quantisation; y [M,H]. */
+ORC_EXPORT int oracle_swiglu_rows_fp8(int64_t M, int64_t H, int64_t I, const float *xr,
+                                      const float *Wg, const float *Wu, const float *Wd, float s_x,
+                                      float s_h, float *h_out, float *y) {
+  if (M < 0 || H <= 0 || I <= 0 || !(s_x > 0.0f) || !(s_h > 0.0f)) return -1;
+  if (M == 0) return 0;
+  if (!xr || !Wg || !Wu || !Wd || !y) return -1;
+  double *wg = (double *)malloc(sizeof(double) * (size_t)(I * H));
+  double *wu = (double *)malloc(sizeof(double) * (size_t)(I * H));
+  double *wd = (double *)malloc(sizeof(double) * (size_t)(H * I));
+  double *xt = (double *)malloc(sizeof(double) * (size_t)H);
+  float *hr = (float *)malloc(sizeof(float) * (size_t)I);
+  double *ht = (double *)malloc(sizeof(double) * (size_t)I);
+  int rc = -1;
+  if (!wg || !wu || !wd || !xt || !hr || !ht) goto done;
+  fp8_dequant_d(I * H, Wg, oracle_fp8_tensor_scale(I * H, Wg), wg);
+  fp8_dequant_d(I * H, Wu, oracle_fp8_tensor_scale(I * H, Wu), wu);
+  fp8_dequant_d(H * I, Wd, oracle_fp8_tensor_scale(H * I, Wd), wd);
+  for (int64_t m = 0; m < M; ++m) {
+    fp8_dequant_d(H, xr + m * H, s_x, xt);
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < I; ++i) {
+      double g = 0.0, u = 0.0;
+      for (int64_t h = 0; h < H; ++h) {
+        g += xt[h] * wg[i * H + h];
+        u += xt[h] * wu[i * H + h];
+      }
+      hr[i] = (float)(g / (1.0 + exp(-g)) * u);
+    }
+    if (h_out) memcpy(h_out + m * I, hr, sizeof(float) * (size_t)I);
+    fp8_dequant_d(I, hr, s_h, ht);
+#pragma omp parallel for schedule(static)
+    for (int64_t n = 0; n < H; ++n) {
+      double acc = 0.0;
+      for (int64_t i = 0; i < I; ++i) acc += ht[i] * wd[n * I + i];
+      y[m * H + n] = (float)acc;
+    }
+  }
+  rc = 0;
+done:
+  free(wg);
+  free(wu);
+  free(wd);
+  free(xt);
+  free(hr);
+  free(ht);
   return rc;
 }
 
