@@ -38,7 +38,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="hy3_decode",
                     choices=["hy3_decode", "hy3_prefill", "hy4_skew", "mx", "tiny", "w4a8_decode",
-                             "w4a8"])
+                             "w4a8", "fp8_decode", "fp8"])
     ap.add_argument("--profile-steps", type=int, default=20)
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
@@ -165,10 +165,11 @@ def main():
     # bytes per weight of the routed and the shared experts (MX: + one scale
     # byte per 32); W4A8 keeps its shared expert in MX-fp8
     mxw = w.dtype in ("mxfp8", "w4a8")
-    eb = {"bf16": 2, "f32": 4, "mxfp8": 1, "w4a8": 0.5}[w.dtype]
+    eight = mxw or w.dtype == "fp8"            # 8-bit (or 4-bit) products
+    eb = {"bf16": 2, "f32": 4, "mxfp8": 1, "w4a8": 0.5, "fp8": 1}[w.dtype]
     ebs = 1 if w.dtype == "w4a8" else eb
     sb = (1.0 / 32.0) if mxw else 0.0
-    ab = 1 if mxw else eb                      # bytes per element of h
+    ab = 1 if eight else eb                    # bytes per element of h
     ob = 4 if w.dtype == "f32" else 2
     xb = 4 if w.dtype == "f32" else 2
 
@@ -193,7 +194,7 @@ def main():
     gu_flops = 2.0 * P * 2 * w.I * w.H
     tok_s = T / (ms * 1e-3)
     # MX products run at the fp8 rate (an E2M1 x E4M3 product is priced as fp8)
-    mfma_peak = FP8_PEAK_TFLOPS if mxw else BF16_PEAK_TFLOPS
+    mfma_peak = FP8_PEAK_TFLOPS if eight else BF16_PEAK_TFLOPS
     if w.name == "hy3_prefill":
         roof = {"bound": "mfma", "kernel": "routed gate/up + SwiGLU grouped GEMM",
                 "achieved": round(gu_flops / (gu_ms * 1e-3) / 1e12, 1), "peak": mfma_peak,
@@ -210,7 +211,7 @@ def main():
         "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "mxfp8-e4m3",
-                  "w4a8": "mxfp4-e2m1 x mxfp8-e4m3"}[w.dtype],
+                  "w4a8": "mxfp4-e2m1 x mxfp8-e4m3", "fp8": "fp8-e4m3 per-tensor"}[w.dtype],
         "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
         "config": {"workload": w.name, "tokens": T, "hidden": w.H, "experts": w.E,
                    "top_k": w.k, "inter": w.I, "shared_inter": w.Is,
@@ -277,7 +278,9 @@ def main():
         def oracle_tokens(toks):
             oracle.layer_forward_tokens(toks, x32, Wr, bias, lambda e: (Wg[e], Wu[e], Wd[e]),
                                         shared, k=w.k, rho=w.rho, route_norm=w.route_norm,
-                                        mx={"mxfp8": 1, "w4a8": 2}.get(w.dtype, 0))
+                                        mx={"mxfp8": 1, "w4a8": 2}.get(w.dtype, 0),
+                                        fp8=((w.fp8_x_scale, w.fp8_h_scale, w.fp8_sh_h_scale)
+                                             if w.dtype == "fp8" else None))
 
         # a bounded sample: the first n tokens of the batch (all of them when
         # the batch is small), evaluated `reps` times back to back

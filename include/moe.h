@@ -62,8 +62,9 @@ typedef enum moe_dtype {
   MOE_F32 = 0,   /* IEEE binary32                                           */
   MOE_BF16 = 1,  /* bfloat16, round-to-nearest-even on every store          */
   MOE_MXFP8 = 2, /* OCP MX: E4M3 (FN) elements, one E8M0 scale per 32       */
-  MOE_MXFP4 = 3  /* OCP MX: E2M1 elements (two per byte, low nibble first),
+  MOE_MXFP4 = 3, /* OCP MX: E2M1 elements (two per byte, low nibble first),
                     one E8M0 scale per 32; expert weights only (W4A8)      */
+  MOE_FP8 = 4    /* E4M3 (FN) with one static fp32 scale per tensor        */
 } moe_dtype;
 
 /* Layer description (host struct).  Field names follow HYV3Config (Hy3 guide,
@@ -78,6 +79,15 @@ typedef enum moe_dtype {
  *                       E2M1 round-to-nearest-even, saturating at 6), the
  *                       shared expert MX-fp8 (W8A8), activations MX-fp8 as
  *                       above; bf16 output
+ *   (BF16, FP8, BF16)   static per-tensor FP8 W8A8 (the FP8 checkpoints of the
+ *                       Hy3 guide, section 2, and the Hy4 tutorial's w8a8
+ *                       weights): every expert weight matrix has one fp32
+ *                       scale max|w| / 448 (computed by moe_pack_experts);
+ *                       x and h are quantised with the fixed activation
+ *                       scales fp8_x_scale / fp8_h_scale / fp8_sh_h_scale;
+ *                       codes are E4M3 of fp32(v / scale), round to nearest
+ *                       even, saturating; products are scaled by weight scale
+ *                       x activation scale after fp32 accumulation
  * The router always runs in fp32 on the unquantised x. */
 typedef struct moe_desc {
   int32_t hidden;                /* H                                        */
@@ -90,6 +100,10 @@ typedef struct moe_desc {
   int32_t act_dtype;             /* moe_dtype of x                           */
   int32_t expert_dtype;          /* moe_dtype of the packed expert weights   */
   int32_t out_dtype;             /* moe_dtype of y, shared output and out    */
+  /* static activation scales (> 0), read only when expert_dtype == MOE_FP8:
+   * x (routed and shared experts), the routed SwiGLU output h, and the
+   * shared expert's h */
+  float fp8_x_scale, fp8_h_scale, fp8_sh_h_scale;
 } moe_desc;
 
 /* Device pointers to the layer's weights (host struct). */
@@ -98,7 +112,8 @@ typedef struct moe_weights {
   const float *router_bias;        /* [E] fp32 logit bias, or NULL          */
   const void *gate_up;             /* routed gate+up, packed (moe_pack_experts) */
   const void *down;                /* routed down, packed                   */
-  const uint8_t *gate_up_scale;    /* MX only: packed E8M0 scales, else NULL */
+  const uint8_t *gate_up_scale;    /* MX: packed E8M0 scales; FP8: fp32 per-tensor
+                                      scales [E][2] (gate, up), down [E]; else NULL */
   const uint8_t *down_scale;
   const void *sh_gate_up;          /* shared expert, packed with shared = 1 */
   const void *sh_down;
@@ -131,8 +146,9 @@ MOE_API size_t moe_workspace_bytes(const moe_desc *desc /* host */, int32_t T, i
 
 /* Packed weight sizes in bytes.  shared: 0 routed experts, 1 shared expert.
  * which: MOE_PACK_GATE_UP, MOE_PACK_DOWN, MOE_PACK_GATE_UP_SCALE,
- * MOE_PACK_DOWN_SCALE (scales are 0 bytes unless expert_dtype is MX-fp8 or
- * MXFP4; the shared expert of an MXFP4 layer is packed as MX-fp8). */
+ * MOE_PACK_DOWN_SCALE (scales are 0 bytes unless expert_dtype is MX-fp8,
+ * MXFP4 or FP8; the shared expert of an MXFP4 layer is packed as MX-fp8;
+ * FP8 scales are fp32, 2 per expert for gate/up and 1 for down). */
 enum { MOE_PACK_GATE_UP = 0, MOE_PACK_DOWN = 1, MOE_PACK_GATE_UP_SCALE = 2,
        MOE_PACK_DOWN_SCALE = 3 };
 MOE_API size_t moe_packed_bytes(const moe_desc *desc /* host */, int shared, int which);
@@ -160,6 +176,12 @@ MOE_API moe_status moe_pack_experts(const moe_desc *desc /* host */, int shared,
  * = E4M3 round-to-nearest-even of v / 2^X saturated to +-448. */
 MOE_API moe_status moe_mx_quantize(const void *src, int src_dtype, int64_t rows, int64_t cols,
                            uint8_t *q, uint8_t *scale, void *stream);
+
+/* Static per-tensor FP8 quantisation of n elements (n a multiple of 8):
+ * q[i] = E4M3 (FN) of fp32(src[i] / scale), round to nearest even,
+ * saturating to +-448.  src_dtype MOE_F32 or MOE_BF16; scale > 0 (host). */
+MOE_API moe_status moe_fp8_quantize(const void *src, int src_dtype, int64_t n, float scale,
+                            uint8_t *q, void *stream);
 
 /* Gating (Hy3 guide, section 1 and section 8.5 "Gating"; HunyuanImage-3.0
  * article part 3: the gate yields expert_index and topk_weight).

@@ -16,13 +16,14 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("MOE_LIBMOE") or os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
-MOE_F32, MOE_BF16, MOE_MXFP8, MOE_MXFP4 = 0, 1, 2, 3
+MOE_F32, MOE_BF16, MOE_MXFP8, MOE_MXFP4, MOE_FP8 = 0, 1, 2, 3, 4
 MOE_WS_ROUTE, MOE_WS_PERMUTE, MOE_WS_GROUPED_FFN, MOE_WS_SHARED_FFN, MOE_WS_LAYER = range(5)
 MOE_PACK_GATE_UP, MOE_PACK_DOWN, MOE_PACK_GATE_UP_SCALE, MOE_PACK_DOWN_SCALE = range(4)
 
 # every symbol include/moe.h declares
 EXPORTS = ("moe_ctx_create", "moe_ctx_destroy", "moe_status_string", "moe_ctx_last_error",
            "moe_workspace_bytes", "moe_packed_bytes", "moe_pack_experts", "moe_mx_quantize",
+           "moe_fp8_quantize",
            "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
            "moe_layer_ws_topk", "moe_ctx_set_profiling", "moe_ctx_stage_ms")
 STAGES = ("route", "mx_quant", "permute", "gate_up", "down", "shared_gate_up", "shared_down",
@@ -34,7 +35,9 @@ class MoeDesc(ctypes.Structure):
                 ("top_k", ctypes.c_int32), ("inter", ctypes.c_int32),
                 ("shared_inter", ctypes.c_int32), ("router_scaling_factor", ctypes.c_float),
                 ("route_norm", ctypes.c_int32), ("act_dtype", ctypes.c_int32),
-                ("expert_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32)]
+                ("expert_dtype", ctypes.c_int32), ("out_dtype", ctypes.c_int32),
+                ("fp8_x_scale", ctypes.c_float), ("fp8_h_scale", ctypes.c_float),
+                ("fp8_sh_h_scale", ctypes.c_float)]
 
 
 class MoeWeights(ctypes.Structure):
@@ -73,6 +76,7 @@ def lib():
             "moe_packed_bytes": ([DP, ctypes.c_int, ctypes.c_int], S),
             "moe_pack_experts": ([DP, ctypes.c_int, ctypes.c_int] + [P] * 8, ctypes.c_int),
             "moe_mx_quantize": ([P, ctypes.c_int, I64, I64, P, P, P], ctypes.c_int),
+            "moe_fp8_quantize": ([P, ctypes.c_int, I64, ctypes.c_float, P, P], ctypes.c_int),
             "moe_route": ([P, DP, P, I32, P, P, P, P, P, S, P], ctypes.c_int),
             "moe_permute": ([P, DP, P, I32, P, P, P, P, P, S, P], ctypes.c_int),
             "moe_grouped_ffn": ([P, DP, WP, ctypes.c_int, P, I32, P, P, P, P, S, P], ctypes.c_int),
@@ -152,6 +156,10 @@ def moe_pack_experts(desc, shared, src_dtype, gate, up, down, gate_up_out, down_
 def moe_mx_quantize(src, src_dtype, rows, cols, q, scale, stream=None):
     _check(lib().moe_mx_quantize(_ptr(src), src_dtype, rows, cols, _ptr(q), _ptr(scale),
                                  _stream(stream)))
+
+
+def moe_fp8_quantize(src, src_dtype, n, scale, q, stream=None):
+    _check(lib().moe_fp8_quantize(_ptr(src), src_dtype, n, scale, _ptr(q), _stream(stream)))
 
 
 def moe_route(ctx, desc, x, T, router_w, router_bias, topk_idx, topk_w, ws, ws_bytes,

@@ -45,7 +45,8 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
 int fmt_of(int dtype) {
   return dtype == MOE_F32 ? FMT_F32
          : dtype == MOE_BF16 ? FMT_BF16
-         : dtype == MOE_MXFP4 ? FMT_MX4 : FMT_MX8;
+         : dtype == MOE_MXFP4 ? FMT_MX4
+         : dtype == MOE_FP8 ? FMT_FP8 : FMT_MX8;
 }
 size_t elem_bytes(int dtype) { return dtype == MOE_F32 ? 4 : dtype == MOE_BF16 ? 2 : 1; }
 int chunk_elems(int dtype) { return dtype == MOE_F32 ? 64 : dtype == MOE_BF16 ? 128 : 256; }
@@ -63,8 +64,13 @@ int weight_fmt(const moe_desc *d, int shared) {
 }
 // Bytes of one packed weight block (16 rows x one K chunk).
 size_t wblock(int fmt) { return fmt == FMT_MX4 ? 2048 : kBlockBytes; }
+// Static per-tensor FP8 experts: x and h are E4M3 under fixed scales.
+bool fp8_act(const moe_desc *d) { return d->expert_dtype == MOE_FP8; }
 // Bytes per activation element in the experts' input format (x, h).
-size_t act_bytes(const moe_desc *d) { return mx_act(d) ? 1 : elem_bytes(d->expert_dtype); }
+size_t act_bytes(const moe_desc *d) {
+  return (mx_act(d) || fp8_act(d)) ? 1 : elem_bytes(d->expert_dtype);
+}
+bool good_scale(float v) { return v > 0.0f && v < 3.0e38f; }
 
 // Shape and dtype checks shared by every entry point.
 moe_status check_desc(const moe_desc *d) {
@@ -74,15 +80,20 @@ moe_status check_desc(const moe_desc *d) {
     return MOE_ERR_INVALID_ARG;
   if (d->route_norm != 0 && d->route_norm != 1) return MOE_ERR_INVALID_ARG;
   for (int v : {d->act_dtype, d->expert_dtype, d->out_dtype})
-    if (v < MOE_F32 || v > MOE_MXFP4) return MOE_ERR_INVALID_ARG;
+    if (v < MOE_F32 || v > MOE_FP8) return MOE_ERR_INVALID_ARG;
   const bool f32 = d->act_dtype == MOE_F32 && d->expert_dtype == MOE_F32 && d->out_dtype == MOE_F32;
   const bool b16 = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_BF16 && d->out_dtype == MOE_BF16;
   const bool mx = d->act_dtype == MOE_BF16 && (d->expert_dtype == MOE_MXFP8 ||
                                               d->expert_dtype == MOE_MXFP4) &&
                   d->out_dtype == MOE_BF16;
-  if (!(f32 || b16 || mx)) return MOE_ERR_UNSUPPORTED;
+  const bool f8 = d->act_dtype == MOE_BF16 && d->expert_dtype == MOE_FP8 &&
+                  d->out_dtype == MOE_BF16;
+  if (!(f32 || b16 || mx || f8)) return MOE_ERR_UNSUPPORTED;
+  if (f8 && !(good_scale(d->fp8_x_scale) && good_scale(d->fp8_h_scale) &&
+              good_scale(d->fp8_sh_h_scale)))
+    return MOE_ERR_INVALID_ARG;
   // K chunks of 256 bytes; output tiles of 256 rows / 16-block groups
-  const int im = mx ? 256 : 128;
+  const int im = (mx || f8) ? 256 : 128;
   if (d->hidden % 256 || d->inter % im || d->shared_inter % im) return MOE_ERR_UNSUPPORTED;
   return MOE_OK;
 }
@@ -121,9 +132,9 @@ Layout layout(const moe_desc *d, int T, int which) {
   if (which == MOE_WS_PERMUTE || layer) L.perm = take(permute_ws_bytes(T, (int)E));
   const bool routed = which == MOE_WS_GROUPED_FFN || layer;
   const bool shared = (which == MOE_WS_SHARED_FFN || layer) && Is > 0;
-  if (mx && (routed || shared)) {
+  if ((mx || fp8_act(d)) && (routed || shared)) {
     L.xq = take((size_t)T * H);
-    L.xs = take((size_t)T * H / 32);
+    if (mx) L.xs = take((size_t)T * H / 32);
   }
   if (routed) {
     L.h = take(P * I * eh);
@@ -202,9 +213,19 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g1.out = h;
   g1.out_scale = hs;
   g1.n_out = I;
+  // static per-tensor FP8: weight scales [E][2], the x scale, and the scale
+  // h is quantised with (then the down GEMM's activation scale)
+  const float sh = shared ? d->fp8_sh_h_scale : d->fp8_h_scale;
+  if (F == FMT_FP8) {
+    g1.w_tscale = (const float *)(shared ? w->sh_gate_up_scale : w->gate_up_scale);
+    g1.w_scale = nullptr;
+    g1.a_tscale = d->fp8_x_scale;
+    g1.out_tscale = sh;
+  }
   hipError_t err;
   if (tm && (err = tm->start(st1, s)) != hipSuccess) return err;
-  // the SwiGLU output h is the down GEMM's input: MX-fp8 for MX experts
+  // the SwiGLU output h is the down GEMM's input: MX-fp8 for MX experts,
+  // E4M3 under its static scale for FP8
   err = launch_grouped_gemm(g1, F, EPI_SWIGLU, mx_act(d) ? FMT_MX8 : F, rows, s);
   if (err != hipSuccess) return err;
   if (tm && (err = tm->stop(st1, s)) != hipSuccess) return err;
@@ -230,6 +251,11 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g2.out = y;
   g2.out_scale = nullptr;
   g2.n_out = H;
+  if (F == FMT_FP8) {
+    g2.w_tscale = (const float *)(shared ? w->sh_down_scale : w->down_scale);
+    g2.w_scale = nullptr;
+    g2.a_tscale = sh;
+  }
   if (tm && (err = tm->start(st2, s)) != hipSuccess) return err;
   err = launch_grouped_gemm(g2, F, EPI_PLAIN, fmt_of(d->out_dtype), rows, s);
   if (err != hipSuccess) return err;
@@ -240,7 +266,7 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
 bool weights_ok(const moe_desc *d, const moe_weights *w, int need_router, int need_routed,
                 int need_shared) {
   if (!w) return false;
-  const bool mx = mx_act(d);
+  const bool mx = mx_act(d) || fp8_act(d);     // both need the scale arrays
   if (need_router && !w->router_w) return false;
   if (need_routed && (!w->gate_up || !w->down || (mx && (!w->gate_up_scale || !w->down_scale))))
     return false;
@@ -356,12 +382,13 @@ size_t moe_packed_bytes(const moe_desc *desc, int shared, int which) {
   const int F = weight_fmt(desc, shared);
   const bool mx = mx_act(desc);
   // bytes per 32 weights (E2M1 packs two per byte)
-  const size_t per32 = F == FMT_F32 ? 128 : F == FMT_BF16 ? 64 : F == FMT_MX8 ? 32 : 16;
+  const size_t per32 = F == FMT_F32 ? 128 : F == FMT_BF16 ? 64 : F == FMT_MX4 ? 16 : 32;
+  const bool f8 = F == FMT_FP8;     // fp32 per-tensor scales
   switch (which) {
     case MOE_PACK_GATE_UP: return E * 2 * I * H / 32 * per32;
     case MOE_PACK_DOWN: return E * H * I / 32 * per32;
-    case MOE_PACK_GATE_UP_SCALE: return mx ? E * 2 * I * H / 32 : 0;
-    case MOE_PACK_DOWN_SCALE: return mx ? E * H * I / 32 : 0;
+    case MOE_PACK_GATE_UP_SCALE: return f8 ? E * 2 * sizeof(float) : mx ? E * 2 * I * H / 32 : 0;
+    case MOE_PACK_DOWN_SCALE: return f8 ? E * sizeof(float) : mx ? E * H * I / 32 : 0;
   }
   return 0;
 }
@@ -376,16 +403,31 @@ moe_status moe_pack_experts(const moe_desc *desc, int shared, int src_dtype, con
   const int E = shared ? 1 : desc->num_experts, H = desc->hidden;
   const int I = shared ? desc->shared_inter : desc->inter;
   if (I == 0) return MOE_OK;
-  const bool mx = mx_act(desc);
+  const bool mx = mx_act(desc) || fp8_act(desc);
   if (!gate || !up || !down || !gate_up_out || !down_out) return MOE_ERR_INVALID_ARG;
   if (mx && (!gate_up_scale_out || !down_scale_out)) return MOE_ERR_INVALID_ARG;
   const int F = weight_fmt(desc, shared);
+  const bool f8 = F == FMT_FP8;
   hipStream_t s = (hipStream_t)stream;
   hipError_t err = launch_pack(gate, up, src_dtype == MOE_BF16, E, 2 * I, H, 1, F,
-                               (uint8_t *)gate_up_out, (uint16_t *)gate_up_scale_out, s);
+                               (uint8_t *)gate_up_out,
+                               f8 ? nullptr : (uint16_t *)gate_up_scale_out,
+                               f8 ? (float *)gate_up_scale_out : nullptr, s);
   if (err == hipSuccess)
     err = launch_pack(down, nullptr, src_dtype == MOE_BF16, E, H, I, 0, F, (uint8_t *)down_out,
-                      (uint16_t *)down_scale_out, s);
+                      f8 ? nullptr : (uint16_t *)down_scale_out,
+                      f8 ? (float *)down_scale_out : nullptr, s);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
+}
+
+moe_status moe_fp8_quantize(const void *src, int src_dtype, int64_t n, float scale, uint8_t *q,
+                            void *stream) {
+  if (n < 0 || n % 8 || !good_scale(scale)) return MOE_ERR_INVALID_ARG;
+  if (src_dtype != MOE_F32 && src_dtype != MOE_BF16) return MOE_ERR_INVALID_ARG;
+  if (n == 0) return MOE_OK;
+  if (!src || !q) return MOE_ERR_INVALID_ARG;
+  hipError_t err = launch_fp8_quantize(src, src_dtype == MOE_BF16, n, scale, q,
+                                       (hipStream_t)stream);
   return err == hipSuccess ? MOE_OK : MOE_ERR_DEVICE;
 }
 
@@ -465,6 +507,11 @@ moe_status moe_grouped_ffn(moe_ctx *ctx, const moe_desc *desc, const moe_weights
     if (err != hipSuccess) return device_error(ctx, err, "moe_grouped_ffn");
     xa = base + L.xq;
     xs = (const uint8_t *)base + L.xs;
+  } else if (fp8_act(desc)) {
+    err = launch_fp8_quantize(x, 1, (long long)T * desc->hidden, desc->fp8_x_scale,
+                              (uint8_t *)base + L.xq, s);
+    if (err != hipSuccess) return device_error(ctx, err, "moe_grouped_ffn");
+    xa = base + L.xq;
   }
   err = ffn(desc, w, shared, xa, xs, T, sorted_src, expert_offsets, y,
             base + (shared ? L.sh_h : L.h),
@@ -541,19 +588,25 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
     MOE_TRY(tm.stop(MOE_STAGE_MX_QUANT, s), "timing");
     xa = b + L.xq;
     xs = (const uint8_t *)b + L.xs;
+  } else if (fp8_act(desc)) {
+    MOE_TRY(tm.start(MOE_STAGE_MX_QUANT, s), "timing");
+    MOE_TRY(launch_fp8_quantize(x, 1, (long long)T * H, desc->fp8_x_scale, (uint8_t *)b + L.xq, s),
+            "activation quantisation");
+    MOE_TRY(tm.stop(MOE_STAGE_MX_QUANT, s), "timing");
+    xa = b + L.xq;
   }
   // Shared expert on the side stream.  It needs only the activations.  For
   // larger batches it is started once the routed gate/up GEMM is queued (the
   // input-ready event is recorded after it), so it runs beside the routed
   // down GEMM: beside gating and permutation it slows those short,
   // latency-bound kernels by more than it saves.  For decode-sized batches
-  // (T <= MOE_SHARED_EARLY_T) with MX experts it starts at once, beside
-  // gating and the routed gate/up GEMM: there the routed down GEMM (4- or
-  // 8-bit weights) is shorter than the MX-fp8 shared expert, which would
-  // otherwise lengthen the layer (W4A8 decode 0.398 -> 0.370 ms).  A bf16
-  // decode batch keeps the late start (the early one slows gating, +0.4%).
+  // (T <= MOE_SHARED_EARLY_T) with 8- or 4-bit experts it starts at once,
+  // beside gating and the routed gate/up GEMM: there the routed down GEMM
+  // is shorter than the 8-bit shared expert, which would otherwise lengthen
+  // the layer (W4A8 decode 0.398 -> 0.370 ms).  A bf16 decode batch keeps
+  // the late start (the early one slows gating, +0.4%).
   const bool two = has_shared && ctx->side && ctx->side != s;
-  const bool early = two && mx && T <= MOE_SHARED_EARLY_T;
+  const bool early = two && (mx || fp8_act(desc)) && T <= MOE_SHARED_EARLY_T;
   auto shared_expert = [&]() -> hipError_t {
     hipStream_t ss = two ? ctx->side : s;
     hipError_t e;

@@ -90,12 +90,33 @@ __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 // ----------------------------------------------------------------------------- epilogue
 // acc[n] (n < NB) is one 16-token column of NB consecutive 16-row weight
 // blocks starting at global block nb0.  Lane: token row `row` (stores only if
-// `valid`), features 4 * (lane / 16) + r of each block.
-template <int EPI, int OT, int NB>
-__device__ __forceinline__ void epilogue(const f32x4 (&acc)[NB], int nb0, long long row, bool valid,
-                                         const GemmArgs &g, int lane) {
+// `valid`), features 4 * (lane / 16) + r of each block.  Static per-tensor
+// FP8 (F == FMT_FP8) first multiplies the gate (and plain) sums by fa and the
+// up sums by fb: the product of the expert's weight scale and the
+// activation scale.
+template <int F, int EPI, int OT, int NB>
+__device__ __forceinline__ void epilogue(f32x4 (&acc)[NB], int nb0, long long row, bool valid,
+                                         const GemmArgs &g, int lane, float fa, float fb) {
   const int c4 = 4 * (lane >> 4);
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (F == FMT_FP8) {
+#pragma unroll
+    for (int n = 0; n < NB; ++n)
+      acc[n] *= (EPI == EPI_SWIGLU && (n & 1)) ? fb : fa;
+  }
+  if constexpr (EPI == EPI_SWIGLU && OT == FMT_FP8) {
+    // h codes E4M3(fp32(h / s_h)), four per lane and block pair
+    const float sh = g.out_tscale;
+#pragma unroll
+    for (int q = 0; q < NB / 2; ++q) {
+      uint32_t c = 0;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c |= e4m3_rne((silu(acc[2 * q][r]) * acc[2 * q + 1][r]) / sh) << (8 * r);
+      if (valid) {
+        const long long col = (long long)(nb0 / 2 + q) * 16 + c4;
+        *(uint32_t *)((uint8_t *)g.out + row * g.n_out + col) = c;
+      }
+    }
+  } else if constexpr (EPI == EPI_SWIGLU) {
     // gate block 2q and up block 2q+1 make h columns (nb0/2 + q)*16 + [0,16)
     if constexpr (OT == FMT_MX8) {
       static_assert(NB % 4 == 0, "MX epilogue needs whole 32-column blocks");
@@ -164,6 +185,20 @@ __device__ __forceinline__ void epilogue(const f32x4 (&acc)[NB], int nb0, long l
   }
 }
 
+// Epilogue factors of expert e under static per-tensor FP8 (1 otherwise).
+template <int F, int EPI>
+__device__ __forceinline__ void tensor_factors(const GemmArgs &g, int e, float &fa, float &fb) {
+  fa = fb = 1.0f;
+  if constexpr (F == FMT_FP8) {
+    if constexpr (EPI == EPI_SWIGLU) {
+      fa = g.w_tscale[2 * e] * g.a_tscale;
+      fb = g.w_tscale[2 * e + 1] * g.a_tscale;
+    } else {
+      fa = fb = g.w_tscale[e] * g.a_tscale;
+    }
+  }
+}
+
 __device__ __forceinline__ long long token_of(const GemmArgs &g, int r) {
   return g.sorted_src ? (long long)(g.sorted_src[r] / g.k_route) : (long long)r;
 }
@@ -195,6 +230,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   if (g.offsets) { s0 = g.offsets[e]; s1 = g.offsets[e + 1]; }
   else { s0 = 0; s1 = g.rows; }
   if (s1 <= s0 || (g.split > 0 && s1 - s0 > g.split)) return;
+  float fa, fb;
+  tensor_factors<F, EPI>(g, e, fa, fb);
   const int nb0 = (KSW == 4) ? grp * NW : (grp * 4 + wave) * NW;
   const int kcn = g.K / FmtInfo<F>::chunk_elems;     // chunks along K
   const int k0 = (KSW == 4) ? wave : 0;
@@ -316,7 +353,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
           for (int n = 0; n < NW; ++n) col[n] = acc[n][i];
           const int r = mbase + 16 * i + (lane & 15);
-          epilogue<EPI, OT, NW>(col, nb0, r, r < s1, g, lane);
+          epilogue<F, EPI, OT, NW>(col, nb0, r, r < s1, g, lane, fa, fb);
         }
       }
       __syncthreads();
@@ -327,7 +364,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
         for (int n = 0; n < NW; ++n) col[n] = acc[n][i];
         const int r = mbase + 16 * i + (lane & 15);
-        epilogue<EPI, OT, NW>(col, nb0, r, r < s1, g, lane);
+        epilogue<F, EPI, OT, NW>(col, nb0, r, r < s1, g, lane, fa, fb);
       }
     }
   }
@@ -468,6 +505,8 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
 #endif
   int e, row0, row_end, nt;
   tile_locate<TM, MOE_TILE_GM>(g, cum, ntn, logical, e, row0, row_end, nt);
+  float fa, fb;
+  tensor_factors<F, EPI>(g, e, fa, fb);
 
   const int kcn = g.K / FmtInfo<F>::chunk_elems;
   const int nstage = 2 * kcn;
@@ -656,7 +695,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
 #pragma unroll
     for (int n = 0; n < NBW; ++n) col[n] = acc[n][m];
     const int r = row0 + (wm * MBW + m) * 16 + (lane & 15);
-    epilogue<EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane);
+    epilogue<F, EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane, fa, fb);
   }
 }
 
@@ -724,7 +763,7 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     hipError_t err = launch_skinny<F, EPI, OT, HNW, MOE_HYB_MB, 1>(g, segs, stream);
     if (err != hipSuccess) return err;
   }
-  if constexpr (is_mx<F>) {
+  if constexpr (is_mx<F> || F == FMT_FP8) {
     return launch_tile<F, EPI, OT, 4, 1, MOE_TILE_TM_MX / 16, 1, MOE_TILE_OCC_MX>(g, total_rows,
                                                                                   stream);
   } else {
@@ -752,6 +791,11 @@ hipError_t launch_grouped_gemm(const GemmArgs &g, int fmt, int epi, int out_fmt,
   if (fmt == FMT_MX8) {
     if (epi == EPI_SWIGLU) return run_gemm<FMT_MX8, EPI_SWIGLU, FMT_MX8>(g, total_rows, stream);
     if (out_fmt == FMT_BF16) return run_gemm<FMT_MX8, EPI_PLAIN, FMT_BF16>(g, total_rows, stream);
+  }
+  if (fmt == FMT_FP8) {
+    // static per-tensor FP8: h is E4M3 under its own static scale
+    if (epi == EPI_SWIGLU) return run_gemm<FMT_FP8, EPI_SWIGLU, FMT_FP8>(g, total_rows, stream);
+    if (out_fmt == FMT_BF16) return run_gemm<FMT_FP8, EPI_PLAIN, FMT_BF16>(g, total_rows, stream);
   }
   if (fmt == FMT_MX4) {
     // E2M1 weights, MX-fp8 tokens; the SwiGLU output is MX-fp8 like the input

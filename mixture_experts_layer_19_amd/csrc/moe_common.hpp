@@ -59,14 +59,16 @@ typedef __attribute__((ext_vector_type(8))) int i32x8;
 typedef __attribute__((ext_vector_type(4))) int i32x4;
 
 // Weight formats.  FMT_MX4 is MXFP4 (E2M1) weights multiplied with MX-fp8
-// activations; every other format uses the same type on both sides.
-enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MX8 = 2, FMT_MX4 = 3 };
+// activations; FMT_FP8 is E4M3 with one static scale per tensor (applied in
+// the epilogue); every other format uses the same type on both sides.
+enum Fmt { FMT_F32 = 0, FMT_BF16 = 1, FMT_MX8 = 2, FMT_MX4 = 3, FMT_FP8 = 4 };
 
 template <int F> struct FmtInfo;
 template <> struct FmtInfo<FMT_F32> { static constexpr int elem_bytes = 4, chunk_elems = 64; };
 template <> struct FmtInfo<FMT_BF16> { static constexpr int elem_bytes = 2, chunk_elems = 128; };
 template <> struct FmtInfo<FMT_MX8> { static constexpr int elem_bytes = 1, chunk_elems = 256; };
 template <> struct FmtInfo<FMT_MX4> { static constexpr int elem_bytes = 1, chunk_elems = 256; };
+template <> struct FmtInfo<FMT_FP8> { static constexpr int elem_bytes = 1, chunk_elems = 256; };
 
 // format of the token-side operand for weight format F
 template <int F> constexpr int tok_fmt = (F == FMT_MX4) ? FMT_MX8 : F;
@@ -220,6 +222,11 @@ __device__ __forceinline__ void mfma_half(f32x4 &acc, const i32x4 &w0, const i32
     const i32x8 b = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 4, 0, WSEL, (int)ws, TSEL,
                                                            (int)ts);
+  } else if constexpr (F == FMT_FP8) {
+    // per-tensor scales are applied in the epilogue: unit block scales (127)
+    const i32x8 a = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
+    const i32x8 b = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, acc, 0, 0, 0, 127, 0, 127);
   } else {
     const i32x8 a = __builtin_shufflevector(w0, w1, 0, 1, 2, 3, 4, 5, 6, 7);
     const i32x8 b = __builtin_shufflevector(t0, t1, 0, 1, 2, 3, 4, 5, 6, 7);
@@ -240,6 +247,10 @@ template <>
 struct Frag<FMT_MX8> {
   i32x8 v;
 };
+template <>
+struct Frag<FMT_FP8> {
+  i32x8 v;
+};
 // E2M1 weights: one 16-byte piece per half-chunk
 template <>
 struct Frag<FMT_MX4> {
@@ -249,7 +260,7 @@ struct Frag<FMT_MX4> {
 template <int F>
 __device__ __forceinline__ Frag<F> make_frag(const i32x4 &a, const i32x4 &b) {
   Frag<F> f;
-  if constexpr (F == FMT_MX8) {
+  if constexpr (F == FMT_MX8 || F == FMT_FP8) {
     f.v = __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7);
   } else if constexpr (F == FMT_MX4) {
     f.v = a;
@@ -273,6 +284,8 @@ __device__ __forceinline__ void mfma_frag(f32x4 &acc, const Frag<F> &w, const Fr
     const i32x8 a = __builtin_shufflevector(w.v, z, 0, 1, 2, 3, 4, 5, 6, 7);
     acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, t.v, acc, 4, 0, WSEL, (int)ws, 0,
                                                            (int)ts);
+  } else if constexpr (F == FMT_FP8) {
+    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.v, t.v, acc, 0, 0, 0, 127, 0, 127);
   } else {
     mfma_half<F>(acc, w.p0, w.p1, t.p0, t.p1, ws, ts);
   }

@@ -31,6 +31,12 @@ struct GemmArgs {
   int mt_upper;               // tile kernel: m-tiles in the grid
   int split;                  // > 0: the streaming kernel takes segments of at most
                               // `split` rows and the tiled kernel the longer ones
+  // static per-tensor FP8 only: weight scales per expert ([E][2] gate, up for
+  // SwiGLU; [E] otherwise), the token-side activation scale, and the scale
+  // the SwiGLU output is quantised with
+  const float *w_tscale;
+  float a_tscale;
+  float out_tscale;
 };
 
 enum Epi { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
@@ -59,10 +65,17 @@ hipError_t launch_combine(const void *y, int y_fmt, const int32_t *dest, const f
 hipError_t launch_mx_quantize(const void *src, int src_is_bf16, long long rows, long long cols,
                               uint8_t *q, uint8_t *scale, hipStream_t stream);
 
+// E4M3 codes of fp32(src / scale) for n elements (static per-tensor FP8).
+hipError_t launch_fp8_quantize(const void *src, int src_is_bf16, long long n, float scale,
+                               uint8_t *q, hipStream_t stream);
+
 // Pack [E][rows][K] sources (gate/up interleaved when gate_up != 0) into the
 // block layout of fmt.  src_is_bf16 selects the source element type.
+// Static per-tensor FP8: tscale receives each source matrix's scale
+// max|w| / 448 ([E][2] gate, up when gate_up != 0, else [E]) before the
+// codes are written.
 hipError_t launch_pack(const void *a, const void *b, int src_is_bf16, int E, int N, int K,
-                       int gate_up, int fmt, uint8_t *out, uint16_t *scale_out,
+                       int gate_up, int fmt, uint8_t *out, uint16_t *scale_out, float *tscale,
                        hipStream_t stream);
 
 }  // namespace moe

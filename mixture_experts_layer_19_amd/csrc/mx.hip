@@ -93,6 +93,59 @@ hipError_t launch_mx_quantize(const void *src, int src_is_bf16, long long rows, 
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------------------- static FP8
+// Static per-tensor FP8 (the FP8 / w8a8 checkpoints of the Hy3 and Hy4
+// families): one fp32 scale per weight tensor, max|w| / 448, and fixed
+// activation scales; codes are E4M3 of fp32(v / scale).
+// E4M3 codes of fp32(src / scale): one thread per 8 elements (n % 8 == 0).
+template <bool BF16>
+__global__ __launch_bounds__(256) void fp8_quantize_kernel(const void *__restrict__ src,
+                                                           long long n8, float scale,
+                                                           uint8_t *__restrict__ q) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= n8) return;
+  uint32_t c[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) c[j >> 2] |= e4m3_rne(load_src<BF16>(src, 8 * i + j) / scale) << (8 * (j & 3));
+  *(uint2 *)(q + 8 * i) = make_uint2(c[0], c[1]);
+}
+
+hipError_t launch_fp8_quantize(const void *src, int src_is_bf16, long long n, float scale,
+                               uint8_t *q, hipStream_t stream) {
+  if (n <= 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  const long long n8 = n / 8;
+  const unsigned grid = (unsigned)((n8 + 255) / 256);
+  if (src_is_bf16)
+    fp8_quantize_kernel<true><<<grid, 256, 0, stream>>>(src, n8, scale, q);
+  else
+    fp8_quantize_kernel<false><<<grid, 256, 0, stream>>>(src, n8, scale, q);
+  return hipGetLastError();
+}
+
+// Per-tensor weight scale of each source matrix: workgroup m reduces matrix
+// m (m = e * nmat + j; j selects source a or b) of `elems` elements to its
+// largest magnitude and writes max / 448 (1 for an all-zero matrix).
+template <bool BF16>
+__global__ __launch_bounds__(256) void fp8_tensor_scale_kernel(const void *__restrict__ a,
+                                                               const void *__restrict__ b,
+                                                               int nmat, long long elems,
+                                                               float *__restrict__ tscale) {
+  const int m = blockIdx.x, e = m / nmat, j = m % nmat;
+  const void *src = j ? b : a;
+  const long long base = (long long)e * elems;
+  float am = 0.0f;
+  for (long long i = threadIdx.x; i < elems; i += 256) am = fmaxf(am, fabsf(load_src<BF16>(src, base + i)));
+  __shared__ float red[256];
+  red[threadIdx.x] = am;
+  __syncthreads();
+  for (int w = 128; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) tscale[m] = red[0] == 0.0f ? 1.0f : red[0] / 448.0f;
+}
+
 // ----------------------------------------------------------------------------- weights
 // One thread per (expert, virtual row, K chunk): it converts the row's 256
 // chunk bytes and scatters them into the fragment block -- piece p of lane
@@ -103,7 +156,8 @@ template <bool BF16, int F>
 __global__ __launch_bounds__(256) void pack_kernel(const void *__restrict__ a,
                                                    const void *__restrict__ b, int E, int N, int K,
                                                    int gate_up, uint8_t *__restrict__ out,
-                                                   uint16_t *__restrict__ scale_out) {
+                                                   uint16_t *__restrict__ scale_out,
+                                                   const float *__restrict__ tscale) {
   constexpr int CE = FmtInfo<F>::chunk_elems;
   constexpr int EB = FmtInfo<F>::elem_bytes;
   const int nbtot = N / 16, kcn = K / CE;
@@ -147,15 +201,30 @@ __global__ __launch_bounds__(256) void pack_kernel(const void *__restrict__ a,
       scale_out[(((long long)e * nbtot + nb) * kcn + kc) * 64 + r16 + 16 * g] =
           (uint16_t)(sc[0] | (sc[1] << 8));
     }
-  } else if constexpr (F == FMT_MX8) {
+  } else if constexpr (F == FMT_MX8 || F == FMT_FP8) {
     uint32_t sc[8];
     uint32_t codes[8][8];
+    if constexpr (F == FMT_FP8) {
+      // one scale for the whole source matrix (gate or up of the expert)
+      const float ts = tscale[gate_up ? 2 * e + (nb & 1) : e];
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      float vals[32];
+      for (int m = 0; m < 8; ++m)
 #pragma unroll
-      for (int i = 0; i < 32; ++i) vals[i] = load_src<BF16>(src, base + 32 * m + i);
-      mx_block(vals, codes[m], sc[m]);
+        for (int w = 0; w < 8; ++w) {
+          uint32_t c = 0;
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            c |= e4m3_rne(load_src<BF16>(src, base + 32 * m + 4 * w + q) / ts) << (8 * q);
+          codes[m][w] = c;
+        }
+    } else {
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        float vals[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) vals[i] = load_src<BF16>(src, base + 32 * m + i);
+        mx_block(vals, codes[m], sc[m]);
+      }
     }
     // chunk byte o lives in MX block o / 32, code word (o % 32) / 4
 #pragma unroll
@@ -166,8 +235,9 @@ __global__ __launch_bounds__(256) void pack_kernel(const void *__restrict__ a,
         const uint32_t *c = &codes[o >> 5][(o & 31) >> 2];
         *(uint4 *)(blk + p * 1024 + (r16 + 16 * g) * 16) = make_uint4(c[0], c[1], c[2], c[3]);
       }
-      scale_out[(((long long)e * nbtot + nb) * kcn + kc) * 64 + r16 + 16 * g] =
-          (uint16_t)(sc[g] | (sc[4 + g] << 8));
+      if constexpr (F == FMT_MX8)
+        scale_out[(((long long)e * nbtot + nb) * kcn + kc) * 64 + r16 + 16 * g] =
+            (uint16_t)(sc[g] | (sc[4 + g] << 8));
     }
   } else {
 #pragma unroll
@@ -192,25 +262,38 @@ __global__ __launch_bounds__(256) void pack_kernel(const void *__restrict__ a,
 }
 
 hipError_t launch_pack(const void *a, const void *b, int src_is_bf16, int E, int N, int K,
-                       int gate_up, int fmt, uint8_t *out, uint16_t *scale_out,
+                       int gate_up, int fmt, uint8_t *out, uint16_t *scale_out, float *tscale,
                        hipStream_t stream) {
   int ce = fmt == FMT_F32 ? 64 : (fmt == FMT_BF16 ? 128 : 256);
-  if (fmt < FMT_F32 || fmt > FMT_MX4) return hipErrorInvalidValue;
+  if (fmt < FMT_F32 || fmt > FMT_FP8) return hipErrorInvalidValue;
   const long long total = (long long)E * N * (K / ce);
   if (total <= 0) return hipSuccess;
+  if (fmt == FMT_FP8) {
+    // per-tensor scales first: one workgroup per source matrix
+    const int nmat = gate_up ? 2 : 1;
+    const long long elems = (long long)(N / nmat) * K;
+    if (src_is_bf16)
+      fp8_tensor_scale_kernel<true><<<E * nmat, 256, 0, stream>>>(a, b, nmat, elems, tscale);
+    else
+      fp8_tensor_scale_kernel<false><<<E * nmat, 256, 0, stream>>>(a, b, nmat, elems, tscale);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
   const unsigned grid = (unsigned)((total + 255) / 256);
 #define MOE_PACK(BF, F)                                                                        \
-  pack_kernel<BF, F><<<grid, 256, 0, stream>>>(a, b, E, N, K, gate_up, out, scale_out)
+  pack_kernel<BF, F><<<grid, 256, 0, stream>>>(a, b, E, N, K, gate_up, out, scale_out, tscale)
   if (src_is_bf16) {
     if (fmt == FMT_F32) MOE_PACK(true, FMT_F32);
     else if (fmt == FMT_BF16) MOE_PACK(true, FMT_BF16);
     else if (fmt == FMT_MX8) MOE_PACK(true, FMT_MX8);
-    else MOE_PACK(true, FMT_MX4);
+    else if (fmt == FMT_MX4) MOE_PACK(true, FMT_MX4);
+    else MOE_PACK(true, FMT_FP8);
   } else {
     if (fmt == FMT_F32) MOE_PACK(false, FMT_F32);
     else if (fmt == FMT_BF16) MOE_PACK(false, FMT_BF16);
     else if (fmt == FMT_MX8) MOE_PACK(false, FMT_MX8);
-    else MOE_PACK(false, FMT_MX4);
+    else if (fmt == FMT_MX4) MOE_PACK(false, FMT_MX4);
+    else MOE_PACK(false, FMT_FP8);
   }
 #undef MOE_PACK
   return hipGetLastError();

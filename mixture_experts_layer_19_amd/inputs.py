@@ -15,6 +15,13 @@ and the Hy4-preview tutorial, section 1):
   mx           T=4096, H=4096, E=192, k=8, I=Is=1536, MX-fp8 experts
   w4a8_decode  T=64,   H=4096, E=192, k=8, I=Is=1536, MXFP4 routed experts (W4A8)
   w4a8         T=4096, H=4096, E=192, k=8, I=Is=1536, MXFP4 routed experts (W4A8)
+  fp8_decode   T=64,   H=4096, E=192, k=8, I=Is=1536, static per-tensor FP8 (W8A8)
+  fp8          T=4096, H=4096, E=192, k=8, I=Is=1536, static per-tensor FP8 (W8A8)
+
+The static FP8 workloads fix their activation scales (the pages give no
+calibration): x 2^-5 (N(0,1) activations stay below 448 * 2^-5 = 14) and h
+2^-3 for the routed and the shared experts (h stays below 56; about 25
+at most in these workloads).
 
 Distributions: activations N(0,1); router and expert weights N(0, 0.02);
 router weights stay fp32.  Every tensor has its own PCG64 stream derived from
@@ -49,14 +56,18 @@ class Workload:
     k: int
     I: int
     Is: int
-    dtype: str                 # "f32", "bf16", "mxfp8" (expert weights + activations) or
+    dtype: str                 # "f32", "bf16", "mxfp8" (expert weights + activations),
                                # "w4a8" (MXFP4 routed experts, MX-fp8 shared and activations)
+                               # or "fp8" (static per-tensor E4M3 W8A8)
     rho: float = ROUTER_SCALING_FACTOR
     route_norm: bool = True
     zipf_beta: float = 0.0     # 0: no router bias
     seed: int = 0
     x_std: float = 1.0
     w_std: float = 0.02
+    fp8_x_scale: float = 2.0 ** -5      # static activation scales ("fp8" only)
+    fp8_h_scale: float = 2.0 ** -3
+    fp8_sh_h_scale: float = 2.0 ** -3
 
     @property
     def P(self) -> int:
@@ -74,6 +85,9 @@ WORKLOADS = {
     "w4a8_decode": Workload("w4a8_decode", T=64, H=4096, E=192, k=8, I=1536, Is=1536,
                             dtype="w4a8"),
     "w4a8": Workload("w4a8", T=4096, H=4096, E=192, k=8, I=1536, Is=1536, dtype="w4a8"),
+    "fp8_decode": Workload("fp8_decode", T=64, H=4096, E=192, k=8, I=1536, Is=1536,
+                           dtype="fp8"),
+    "fp8": Workload("fp8", T=4096, H=4096, E=192, k=8, I=1536, Is=1536, dtype="fp8"),
 }
 
 

@@ -17,14 +17,17 @@ _DT = {"f32": (B.MOE_F32, B.MOE_F32, B.MOE_F32),
        "bf16": (B.MOE_BF16, B.MOE_BF16, B.MOE_BF16),
        "mxfp8": (B.MOE_BF16, B.MOE_MXFP8, B.MOE_BF16),
        # W4A8: MXFP4 routed experts, MX-fp8 shared expert and activations
-       "w4a8": (B.MOE_BF16, B.MOE_MXFP4, B.MOE_BF16)}
+       "w4a8": (B.MOE_BF16, B.MOE_MXFP4, B.MOE_BF16),
+       # static per-tensor FP8 W8A8
+       "fp8": (B.MOE_BF16, B.MOE_FP8, B.MOE_BF16)}
 
 
 def desc_for(w: I.Workload) -> B.MoeDesc:
     a, e, o = _DT[w.dtype]
     return B.MoeDesc(hidden=w.H, num_experts=w.E, top_k=w.k, inter=w.I, shared_inter=w.Is,
                      router_scaling_factor=w.rho, route_norm=int(w.route_norm), act_dtype=a,
-                     expert_dtype=e, out_dtype=o)
+                     expert_dtype=e, out_dtype=o, fp8_x_scale=w.fp8_x_scale,
+                     fp8_h_scale=w.fp8_h_scale, fp8_sh_h_scale=w.fp8_sh_h_scale)
 
 
 def torch_dtype(moe_dtype: int):
@@ -52,7 +55,7 @@ class DeviceLayer:
         nb = lambda shared, which: B.moe_packed_bytes(d, shared, which)
         self.gate_up = torch.empty(nb(0, B.MOE_PACK_GATE_UP), dtype=u8, device=self.dev)
         self.down = torch.empty(nb(0, B.MOE_PACK_DOWN), dtype=u8, device=self.dev)
-        mx = w.dtype in ("mxfp8", "w4a8")
+        mx = w.dtype in ("mxfp8", "w4a8", "fp8")     # scale arrays
         self.gate_up_s = torch.empty(nb(0, B.MOE_PACK_GATE_UP_SCALE), dtype=u8, device=self.dev) if mx else None
         self.down_s = torch.empty(nb(0, B.MOE_PACK_DOWN_SCALE), dtype=u8, device=self.dev) if mx else None
         self.sh_gate_up = torch.empty(nb(1, B.MOE_PACK_GATE_UP), dtype=u8, device=self.dev)

@@ -11,7 +11,7 @@ from mixture_experts_layer_19_amd import binding as B
 from mixture_experts_layer_19_amd import inputs as I
 from mixture_experts_layer_19_amd.layer import desc_for, to_device
 
-from _gpu import (TOL, classify_routing, oracle_mx, rel_max_err, to_numpy, unpack_blocks,
+from _gpu import (TOL, classify_routing, oracle_ffn, rel_max_err, to_numpy, unpack_blocks,
                   unpack_blocks_e2m1, unpack_scales, virtual_to_gate_up)
 
 pytestmark = pytest.mark.gpu
@@ -56,6 +56,56 @@ def test_mx_quantize_bit_exact(orc, src):
     oq, os_ = orc.mxq(ref)
     np.testing.assert_array_equal(s.cpu().numpy(), os_)
     np.testing.assert_array_equal(q.cpu().numpy(), oq)
+
+
+@pytest.mark.parametrize("src", ["f32", "bf16"])
+def test_fp8_quantize_bit_exact(orc, src):
+    rng = np.random.default_rng(6)
+    n, s = 8 * 4099, 2.0 ** -5
+    v = (rng.standard_normal(n) * np.exp(rng.uniform(-9, 3, n))).astype(np.float32)
+    v[:8] = [14.0, 20.0, -1e6, 0.0, -0.0, 2.0 ** -14, 3.0 * 2.0 ** -15, 1e-30]
+    if src == "bf16":
+        bits = I.bf16_round(v)
+        xin, ref, dt = dev(bits), I.bf16_widen(bits), B.MOE_BF16
+    else:
+        xin, ref, dt = dev(v), v, B.MOE_F32
+    for scale in (s, 0.0123):
+        q = torch.empty(n, dtype=torch.uint8, device="cuda")
+        B.moe_fp8_quantize(xin, dt, n, scale, q)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(q.cpu().numpy(), orc.fp8_quantize(ref, scale))
+
+
+def test_pack_experts_fp8_layout(orc):
+    """Static per-tensor FP8: fp32 scale per matrix and E4M3 codes bit-exact
+    against the oracle, for fp32 and bf16 sources."""
+    w = I.Workload("pack8", T=1, H=512, E=3, k=2, I=256, Is=256, dtype="fp8")
+    d = desc_for(w)
+    masters = [I.expert_master(w, e) for e in range(w.E)]
+    masters[1] = tuple(m * 0 for m in masters[1])          # all-zero expert: scale 1
+    nb = lambda which: B.moe_packed_bytes(d, 0, which)
+    assert nb(B.MOE_PACK_GATE_UP_SCALE) == 2 * 4 * w.E and nb(B.MOE_PACK_DOWN_SCALE) == 4 * w.E
+    u8 = lambda n: torch.empty(n, dtype=torch.uint8, device="cuda")
+    for sdt in (B.MOE_F32, B.MOE_BF16):
+        if sdt == B.MOE_BF16:
+            src = [np.stack([I.bf16_round(m[i]) for m in masters]) for i in range(3)]
+            ref = [I.bf16_widen(a) for a in src]
+        else:
+            src = ref = [np.stack([m[i] for m in masters]) for i in range(3)]
+        gu, dn = u8(nb(B.MOE_PACK_GATE_UP)), u8(nb(B.MOE_PACK_DOWN))
+        gus, dns = u8(nb(B.MOE_PACK_GATE_UP_SCALE)), u8(nb(B.MOE_PACK_DOWN_SCALE))
+        B.moe_pack_experts(d, 0, sdt, dev(src[0]), dev(src[1]), dev(src[2]), gu, dn, gus, dns)
+        torch.cuda.synchronize()
+        sgu = gus.cpu().numpy().view(np.float32).reshape(w.E, 2)
+        sdn = dns.cpu().numpy().view(np.float32)
+        g_b, u_b = virtual_to_gate_up(unpack_blocks(gu.cpu().numpy(), w.E, 2 * w.I, w.H), w.I)
+        d_b = unpack_blocks(dn.cpu().numpy(), w.E, w.H, w.I)
+        for e in range(w.E):
+            for arr, sc, r in ((g_b[e], sgu[e, 0], ref[0][e]), (u_b[e], sgu[e, 1], ref[1][e]),
+                               (d_b[e], sdn[e], ref[2][e])):
+                so = orc.fp8_tensor_scale(r)
+                assert sc == np.float32(so), (e, sc, so)
+                np.testing.assert_array_equal(arr, orc.fp8_quantize(r, so))
 
 
 def test_pack_experts_w4a8_layout(orc):
@@ -338,16 +388,15 @@ def _ffn_case(orc, ctx, w, T, tag, shared=False, idx=None):
                           None if shared else dev(src), None if shared else dev(offs), yt, ws, n)
         torch.cuda.synchronize()
         y = to_numpy(yt)
-        mx = oracle_mx(w.dtype, shared)
         if shared:
-            _, ref = orc.swiglu_rows(x, *I.shared_stored(w), mx=mx)
+            _, ref = oracle_ffn(orc, w, x, I.shared_stored(w), shared=True)
         else:
             ref = np.zeros((P, w.H), np.float32)
             for e in range(w.E):
                 r0, r1 = offs[e], offs[e + 1]
                 if r1 > r0:
                     toks = src[r0:r1] // w.k
-                    _, ref[r0:r1] = orc.swiglu_rows(x[toks], *I.expert_stored(w, e), mx=mx)
+                    _, ref[r0:r1] = oracle_ffn(orc, w, x[toks], I.expert_stored(w, e))
         return rel_max_err(y, ref)
     finally:
         lay.close()
@@ -370,6 +419,9 @@ def _ffn_case(orc, ctx, w, T, tag, shared=False, idx=None):
     ("w4a8", 1024, 1536, 12, 4, 30),    # streaming, MXFP4 weights x MX-fp8 tokens
     ("w4a8", 1024, 1536, 3, 2, 400),    # tiled, W4A8
     ("w4a8", 1024, 1536, 12, 2, 300),   # mixed, W4A8
+    ("fp8", 1024, 1536, 12, 4, 30),     # streaming, static per-tensor FP8
+    ("fp8", 1024, 1536, 3, 2, 400),     # tiled, FP8
+    ("fp8", 1024, 1536, 12, 2, 300),    # mixed, FP8
 ])
 def test_grouped_ffn_parity(orc, ctx, dtype, H, I_, E, k, T):
     w = I.Workload("ffn", T=T, H=H, E=E, k=k, I=I_, Is=I_, dtype=dtype)
@@ -379,11 +431,12 @@ def test_grouped_ffn_parity(orc, ctx, dtype, H, I_, E, k, T):
 
 
 @pytest.mark.parametrize("dtype,T", [("f32", 50), ("f32", 200), ("bf16", 64), ("bf16", 333),
-                                     ("mxfp8", 20), ("mxfp8", 333), ("w4a8", 20)])
+                                     ("mxfp8", 20), ("mxfp8", 333), ("w4a8", 20), ("fp8", 20),
+                                     ("fp8", 333)])
 def test_shared_ffn_parity(orc, ctx, dtype, T):
     # (the shared expert of a W4A8 layer is MX-fp8)
-    Iw = 1536 if dtype in ("mxfp8", "w4a8") else 256
-    H = 1024 if dtype in ("mxfp8", "w4a8") else 512
+    Iw = 1536 if dtype in ("mxfp8", "w4a8", "fp8") else 256
+    H = 1024 if dtype in ("mxfp8", "w4a8", "fp8") else 512
     w = I.Workload("shared", T=T, H=H, E=4, k=2, I=Iw, Is=Iw, dtype=dtype)
     err = _ffn_case(orc, ctx, w, T, tag=2, shared=True)
     print("[shared ffn] %s T=%d rel err %.3g" % (dtype, T, err))

@@ -15,8 +15,8 @@ from mixture_experts_layer_19_amd import binding as B
 from mixture_experts_layer_19_amd import inputs as I
 from mixture_experts_layer_19_amd.layer import DeviceLayer, to_device
 
-from _gpu import (TOL, classify_routing, device_layer, expert_weights_parallel, oracle_mx,
-                  rel_max_err, to_numpy)
+from _gpu import (TOL, classify_routing, device_layer, expert_weights_parallel, oracle_fp8,
+                  oracle_mx, rel_max_err, to_numpy)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,7 +63,7 @@ def _check_layer(orc, name, T=None, full=False, w=None):
     ew = expert_weights_parallel(w, experts)
     ref, o_idx, _, _ = orc.layer_forward_tokens(
         keep, x, Wr, b, lambda e: ew[e], I.shared_stored(w), k=w.k, rho=w.rho,
-        route_norm=w.route_norm, mx=oracle_mx(w.dtype))
+        route_norm=w.route_norm, mx=oracle_mx(w.dtype), fp8=oracle_fp8(w))
     np.testing.assert_array_equal(o_idx, o_idx_all[keep])
     err = rel_max_err(out[keep], ref)
     print("[layer] %s T=%d: %d tokens compared, %d tie flips, rel err %.3g"
@@ -101,6 +101,15 @@ def test_layer_w4a8_sampled(orc):
     _check_layer(orc, "w4a8")
 
 
+def test_layer_fp8_decode_all_tokens(orc):
+    # static per-tensor FP8 W8A8 experts (routed and shared)
+    _check_layer(orc, "fp8_decode", full=True)
+
+
+def test_layer_fp8_sampled(orc):
+    _check_layer(orc, "fp8")
+
+
 @pytest.mark.parametrize("T", [1, 5, 77, 300])
 def test_layer_ragged_token_counts(orc, T):
     _check_layer(orc, "hy3_decode", T=T, full=T <= 77)
@@ -108,12 +117,12 @@ def test_layer_ragged_token_counts(orc, T):
 
 @pytest.mark.parametrize("dtype,E,k,T", [("bf16", 1024, 16, 300), ("f32", 1024, 16, 70),
                                          ("bf16", 1024, 1, 260), ("mxfp8", 1024, 16, 40),
-                                         ("w4a8", 1024, 16, 40)])
+                                         ("w4a8", 1024, 16, 40), ("fp8", 1024, 16, 40)])
 def test_layer_largest_expert_count_and_top_k(orc, dtype, E, k, T):
     # the largest E and k the library accepts (1024, 16), and k = 1, on a
     # narrow layer so the oracle stays quick; every token is compared.  MX
     # needs hidden and intermediate sizes in whole 256-element chunks.
-    H, Iw = (512, 256) if dtype in ("mxfp8", "w4a8") else (256, 128)
+    H, Iw = (512, 256) if dtype in ("mxfp8", "w4a8", "fp8") else (256, 128)
     w = I.Workload("maxes", T=T, H=H, E=E, k=k, I=Iw, Is=Iw, dtype=dtype)
     _check_layer(orc, "maxes", w=w, full=True)
 
