@@ -115,6 +115,14 @@ def test_layer_ragged_token_counts(orc, T):
     _check_layer(orc, "hy3_decode", T=T, full=T <= 77)
 
 
+@pytest.mark.parametrize("name,T", [("w4a8_decode", 1), ("w4a8_decode", 77), ("w4a8_decode", 300),
+                                    ("fp8_decode", 1), ("fp8_decode", 77), ("fp8_decode", 300)])
+def test_layer_ragged_token_counts_8_and_4_bit(orc, name, T):
+    # T <= 64: streaming kernels and the shared expert started before gating;
+    # larger T: short experts streamed, long ones tiled, late start
+    _check_layer(orc, name, T=T, full=T <= 77)
+
+
 @pytest.mark.parametrize("dtype,E,k,T", [("bf16", 1024, 16, 300), ("f32", 1024, 16, 70),
                                          ("bf16", 1024, 1, 260), ("mxfp8", 1024, 16, 40),
                                          ("w4a8", 1024, 16, 40), ("fp8", 1024, 16, 40)])
@@ -137,7 +145,7 @@ def test_layer_zero_tokens_is_a_noop():
     assert torch.all(out == 7.0)
 
 
-@pytest.mark.parametrize("name", ["tiny", "hy3_decode"])
+@pytest.mark.parametrize("name", ["tiny", "hy3_decode", "w4a8_decode", "fp8_decode"])
 def test_layer_is_deterministic_and_stream_independent(name):
     w = I.workload(name)
     lay = device_layer(w)
@@ -156,7 +164,7 @@ def test_layer_is_deterministic_and_stream_independent(name):
     assert torch.equal(a, c)
 
 
-@pytest.mark.parametrize("name", ["tiny", "hy3_decode"])
+@pytest.mark.parametrize("name", ["tiny", "hy3_decode", "w4a8_decode"])
 def test_layer_graph_replay_matches_eager(name):
     # one forward captured as a HIP graph (both streams), replayed on new
     # inputs with eager calls and synchronizations in between: every replay
