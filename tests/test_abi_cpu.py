@@ -119,3 +119,59 @@ def test_null_context_is_rejected(B):
     with pytest.raises(B.MoeError) as ei:
         B.moe_route(None, d, 1, 4, 1, None, 1, 1, 1, 1 << 30)
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
+
+
+def test_w4a8_and_fp8_packed_sizes(B):
+    w4 = _desc(B, expert_dtype=B.MOE_MXFP4)
+    E, I, H = 192, 1536, 4096
+    assert B.moe_packed_bytes(w4, 0, B.MOE_PACK_GATE_UP) == E * 2 * I * H // 2   # E2M1: 2 per byte
+    assert B.moe_packed_bytes(w4, 0, B.MOE_PACK_DOWN) == E * H * I // 2
+    assert B.moe_packed_bytes(w4, 0, B.MOE_PACK_GATE_UP_SCALE) == E * 2 * I * H // 32
+    # the shared expert of a W4A8 layer stays MX-fp8
+    assert B.moe_packed_bytes(w4, 1, B.MOE_PACK_GATE_UP) == 2 * I * H
+    assert B.moe_packed_bytes(w4, 1, B.MOE_PACK_DOWN_SCALE) == H * I // 32
+    f8 = _desc(B, expert_dtype=B.MOE_FP8, fp8_x_scale=2.0 ** -5, fp8_h_scale=0.125,
+               fp8_sh_h_scale=0.125)
+    assert B.moe_packed_bytes(f8, 0, B.MOE_PACK_GATE_UP) == E * 2 * I * H
+    assert B.moe_packed_bytes(f8, 0, B.MOE_PACK_GATE_UP_SCALE) == E * 2 * 4   # fp32 per tensor
+    assert B.moe_packed_bytes(f8, 0, B.MOE_PACK_DOWN_SCALE) == E * 4
+    assert B.moe_packed_bytes(f8, 1, B.MOE_PACK_GATE_UP_SCALE) == 2 * 4
+    # 8-bit activations: the workspace holds 1-byte x and h instead of bf16
+    d16 = _desc(B)
+    assert B.moe_workspace_bytes(f8, 4096, B.MOE_WS_LAYER) < B.moe_workspace_bytes(d16, 4096,
+                                                                                   B.MOE_WS_LAYER)
+
+
+@pytest.mark.parametrize("bad", [dict(fp8_x_scale=0.0), dict(fp8_h_scale=-1.0),
+                                 dict(fp8_sh_h_scale=float("nan")),
+                                 dict(fp8_x_scale=float("inf")), dict(inter=128)])
+def test_fp8_descriptor_checks(B, bad):
+    kw = dict(expert_dtype=B.MOE_FP8, fp8_x_scale=2.0 ** -5, fp8_h_scale=0.125,
+              fp8_sh_h_scale=0.125)
+    kw.update(bad)
+    d = _desc(B, **kw)
+    assert B.moe_packed_bytes(d, 0, B.MOE_PACK_GATE_UP) == 0
+
+
+def test_low_precision_dtype_combinations(B):
+    # MXFP4 and FP8 are expert formats only: not for activations or outputs
+    for kw in (dict(act_dtype=B.MOE_MXFP4, expert_dtype=B.MOE_MXFP4),
+               dict(out_dtype=B.MOE_FP8, expert_dtype=B.MOE_FP8, fp8_x_scale=1.0, fp8_h_scale=1.0,
+                    fp8_sh_h_scale=1.0),
+               dict(act_dtype=B.MOE_F32, expert_dtype=B.MOE_MXFP4)):
+        d = _desc(B, **kw)
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_pack_experts(d, 0, B.MOE_F32, 1, 1, 1, 1, 1, 1, 1)
+        assert ei.value.status == B.MOE_ERR_UNSUPPORTED
+    assert B.moe_packed_bytes(_desc(B, expert_dtype=5), 0, B.MOE_PACK_GATE_UP) == 0
+
+
+def test_fp8_quantize_argument_checks(B):
+    for args in ((1, B.MOE_F32, 12, 1.0, 1),          # n not a multiple of 8
+                 (1, B.MOE_F32, 16, 0.0, 1),          # scale must be > 0
+                 (None, B.MOE_F32, 16, 1.0, 1),
+                 (1, B.MOE_FP8, 16, 1.0, 1)):          # source dtype
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_fp8_quantize(*args)
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    B.moe_fp8_quantize(None, B.MOE_F32, 0, 1.0, None)   # n = 0: no-op
