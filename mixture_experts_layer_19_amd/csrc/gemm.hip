@@ -25,22 +25,31 @@
 #ifndef MOE_TILE_MAP
 #define MOE_TILE_MAP 0
 #endif
-// Dynamic LDS reserved per workgroup of the decode streaming kernel, which
-// uses none: it caps residency at 3 workgroups per CU.  Fewer concurrent
-// weight streams read HBM faster here (6.35 -> 6.5 TB/s), and the shared
-// expert's workgroups on the side stream find free slots instead of waiting
-// for the routed GEMM to drain.
+// Decode streaming kernel: weight blocks per wave, and the dynamic LDS
+// reserved per workgroup (the kernel uses none), which caps its residency.
+// Fewer concurrent weight streams read HBM faster than a full CU, and leave
+// slots for the shared expert's workgroups on the side stream.  Measured at
+// T = 64 (Hy3 shape):
+//  * bf16 and fp32: 2 blocks per wave at 5 workgroups per CU (30000 bytes);
+//    4 blocks at 3 workgroups per CU measured 1.097 ms for the layer against
+//    1.085, and 2 blocks at 3, 4 or 6 workgroups per CU 1.10-1.11 ms;
+//  * 8-bit weights (static FP8, MX-fp8): 4 blocks at 3 workgroups per CU
+//    (45000 bytes); the bf16 setting slows the FP8 gate/up 0.351 -> 0.372 ms;
+//  * E2M1 weights: 8 blocks per wave for the gate/up GEMM, whose blocks are
+//    half as large (0.212 -> 0.205 ms against 4), 2 for the down GEMM, at 5
+//    workgroups per CU (layer 0.367 -> 0.363 ms against 4 blocks at 3).
 #ifndef MOE_SKINNY_LDS_PAD
-#define MOE_SKINNY_LDS_PAD 45000
+#define MOE_SKINNY_LDS_PAD 30000
 #endif
-// streaming kernel at decode sizes: weight blocks per wave, explicit prefetch
+#ifndef MOE_SKINNY_LDS_PAD_8BIT
+#define MOE_SKINNY_LDS_PAD_8BIT 45000
+#endif
 #ifndef MOE_SKINNY_NW
-#define MOE_SKINNY_NW 4
+#define MOE_SKINNY_NW 2
 #endif
-// the same for the gate/up GEMM over E2M1 weights, whose blocks are half as
-// large: eight blocks per wave keep a wave's bytes per chunk at the bf16
-// figure (W4A8 decode gate/up 0.212 -> 0.205 ms; for the down GEMM eight
-// blocks leave too few workgroups and measured slower)
+#ifndef MOE_SKINNY_NW_8BIT
+#define MOE_SKINNY_NW_8BIT 4
+#endif
 #ifndef MOE_SKINNY_NW_MX4
 #define MOE_SKINNY_NW_MX4 8
 #endif
@@ -708,13 +717,14 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
 
 // ----------------------------------------------------------------------------- dispatch
 
+// lds_pad: dynamic LDS per workgroup, which only caps residency.
 template <int F, int EPI, int OT, int NW, int MB, int KSW, int PF = 0>
-static hipError_t launch_skinny(const GemmArgs &g, int segs, hipStream_t stream) {
+static hipError_t launch_skinny(const GemmArgs &g, int segs, hipStream_t stream, int lds_pad = 0) {
   constexpr int BPW = (KSW == 4) ? NW : 4 * NW;
   const int nbtot = g.N / 16;
   if (nbtot % BPW) return hipErrorInvalidValue;
   gemm_skinny_kernel<F, EPI, OT, NW, MB, KSW, PF>
-      <<<segs * (nbtot / BPW), 256, (KSW == 1 && MB == 1) ? MOE_SKINNY_LDS_PAD : 0, stream>>>(g);
+      <<<segs * (nbtot / BPW), 256, lds_pad, stream>>>(g);
   return hipGetLastError();
 }
 
@@ -758,8 +768,17 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     if (per <= 64) return launch_skinny<F, EPI, OT, NWS, 4, 4>(g, 1, stream);
   } else if (g.rows <= 64 * g.k_route) {
     // at most T <= 64 rows per expert: the streaming kernel takes them all
-    constexpr int SNW = (F == FMT_MX4 && EPI == EPI_SWIGLU) ? MOE_SKINNY_NW_MX4 : MOE_SKINNY_NW;
-    if (per <= 16) return launch_skinny<F, EPI, OT, SNW, 1, 1, MOE_SKINNY_PF>(g, segs, stream);
+    constexpr bool eight = (F == FMT_FP8 || F == FMT_MX8);
+    constexpr int SNW0 = (F == FMT_MX4 && EPI == EPI_SWIGLU) ? MOE_SKINNY_NW_MX4
+                         : eight                              ? MOE_SKINNY_NW_8BIT
+                                                              : MOE_SKINNY_NW;
+    const int pad = eight ? MOE_SKINNY_LDS_PAD_8BIT : MOE_SKINNY_LDS_PAD;
+    // a SwiGLU epilogue needs gate/up pairs (2 weight blocks), an
+    // MX-quantising one whole 32-column blocks (4)
+    constexpr int SNW = (EPI == EPI_SWIGLU && OT == FMT_MX8 && SNW0 < 4)   ? 4
+                        : (EPI == EPI_SWIGLU && SNW0 < 2) ? 2
+                                                          : SNW0;
+    if (per <= 16) return launch_skinny<F, EPI, OT, SNW, 1, 1, MOE_SKINNY_PF>(g, segs, stream, pad);
     if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
     return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
   } else {
