@@ -170,7 +170,6 @@ __global__ __launch_bounds__(256) void perm_single_kernel(
   int ev[kMaxChoices];
   if (tid < T) load_choices<KT>(topk_idx, tid, k, ev);
   for (int i = tid; i < E * kPermWords; i += 256) col[i] = 0u;
-  for (int e = tid; e < 1024; e += 256) tot[e] = 0;
   __syncthreads();
   if (tid < T) {
 #pragma unroll
@@ -189,14 +188,32 @@ __global__ __launch_bounds__(256) void perm_single_kernel(
     tot[e] = c;
   }
   __syncthreads();
-  // Hillis-Steele inclusive scan over 1024 entries (E <= 1024).
-  for (int d = 1; d < 1024; d <<= 1) {
-    int v[4];
-    int n = 0;
-    for (int e = tid; e < 1024; e += 256) v[n++] = (e >= d) ? tot[e - d] : 0;
+  // Inclusive scan of the E <= 1024 counts: thread t owns entries 4t..4t+3,
+  // the waves scan their threads' sums with shuffles, and the four wave
+  // totals are added in wave order.
+  {
+    __shared__ int wtot[4];
+    const int lane = tid & 63, wave = tid >> 6;
+    int v[4], run = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = 4 * tid + i;
+      run += (e < E) ? tot[e] : 0;
+      v[i] = run;
+    }
+    int x = run;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(x, d, 64);
+      if (lane >= d) x += y;
+    }
+    if (lane == 63) wtot[wave] = x;
     __syncthreads();
-    n = 0;
-    for (int e = tid; e < 1024; e += 256) tot[e] += v[n++];
+    int before = x - run;
+    for (int w = 0; w < wave; ++w) before += wtot[w];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * tid + i < E) tot[4 * tid + i] = before + v[i];
     __syncthreads();
   }
   for (int e = tid; e <= E; e += 256) offsets[e] = (e == 0) ? 0 : tot[e - 1];
