@@ -74,6 +74,37 @@ __global__ __launch_bounds__(256) void perm_count_kernel(const int32_t *__restri
   }
 }
 
+// Inclusive scan of tot[0, E) in LDS (E <= 1024) by a workgroup of 256
+// threads, called by all of them after the entries are written and a
+// barrier: thread t owns entries 4t..4t+3, the waves scan their threads'
+// sums with shuffles, and the four wave totals are added in wave order.  The
+// workgroup is synchronised again on return.
+__device__ __forceinline__ void block_scan_counts(int32_t *tot, int E) {
+  __shared__ int wtot[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int v[4], run = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = 4 * tid + i;
+    run += (e < E) ? tot[e] : 0;
+    v[i] = run;
+  }
+  int x = run;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d, 64);
+    if (lane >= d) x += y;
+  }
+  if (lane == 63) wtot[wave] = x;
+  __syncthreads();
+  int before = x - run;
+  for (int w = 0; w < wave; ++w) before += wtot[w];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (4 * tid + i < E) tot[4 * tid + i] = before + v[i];
+  __syncthreads();
+}
+
 // Phase 2 (one workgroup): per-expert exclusive scan over blocks, the
 // per-expert counts, and the exclusive scan over experts.
 __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restrict__ blk_count,
@@ -83,9 +114,6 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restric
                                                          int32_t *__restrict__ offsets) {
   __shared__ int32_t tot[1024];
   const int tid = threadIdx.x;
-  // blockDim.x == 256: each thread owns entries tid + 256 i, i < 4.
-  for (int e = tid; e < 1024; e += blockDim.x) tot[e] = 0;
-  __syncthreads();
   for (int e = tid; e < E; e += blockDim.x) {
     // eight block counts are read before any is added, so eight loads are
     // in flight instead of one
@@ -108,16 +136,7 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restric
     tot[e] = run;
   }
   __syncthreads();
-  // Hillis-Steele inclusive scan over 1024 entries (E <= 1024).
-  for (int d = 1; d < 1024; d <<= 1) {
-    int v[4];
-    int n = 0;
-    for (int e = tid; e < 1024; e += blockDim.x) v[n++] = (e >= d) ? tot[e - d] : 0;
-    __syncthreads();
-    n = 0;
-    for (int e = tid; e < 1024; e += blockDim.x) tot[e] += v[n++];
-    __syncthreads();
-  }
+  block_scan_counts(tot, E);
   for (int e = tid; e <= E; e += blockDim.x) offsets[e] = (e == 0) ? 0 : tot[e - 1];
 }
 
@@ -188,34 +207,7 @@ __global__ __launch_bounds__(256) void perm_single_kernel(
     tot[e] = c;
   }
   __syncthreads();
-  // Inclusive scan of the E <= 1024 counts: thread t owns entries 4t..4t+3,
-  // the waves scan their threads' sums with shuffles, and the four wave
-  // totals are added in wave order.
-  {
-    __shared__ int wtot[4];
-    const int lane = tid & 63, wave = tid >> 6;
-    int v[4], run = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = 4 * tid + i;
-      run += (e < E) ? tot[e] : 0;
-      v[i] = run;
-    }
-    int x = run;
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(x, d, 64);
-      if (lane >= d) x += y;
-    }
-    if (lane == 63) wtot[wave] = x;
-    __syncthreads();
-    int before = x - run;
-    for (int w = 0; w < wave; ++w) before += wtot[w];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * tid + i < E) tot[4 * tid + i] = before + v[i];
-    __syncthreads();
-  }
+  block_scan_counts(tot, E);
   for (int e = tid; e <= E; e += 256) offsets[e] = (e == 0) ? 0 : tot[e - 1];
   if (tid >= T) return;
   const int word = tid >> 5;
