@@ -19,6 +19,10 @@
 //    stage.  The m-tile -> (expert, rows) map is computed on the device from
 //    the segment offsets, so no host synchronisation is needed; the grid is
 //    sized from an upper bound and surplus workgroups exit.
+//
+// Both kernels take the weight format as a template parameter: fp32, bf16,
+// MX-fp8, E2M1 weights against MX-fp8 tokens (W4A8), or E4M3 with static
+// per-tensor scales, which the epilogue applies.
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
 

@@ -41,9 +41,11 @@ struct GemmArgs {
 
 enum Epi { EPI_SWIGLU = 0, EPI_PLAIN = 1 };
 
-// fmt: weight/token format (Fmt in moe_common.hpp); out_fmt: FMT_F32,
-// FMT_BF16 or FMT_MX8 (SwiGLU only).  rows_hint: expected rows per segment,
-// used only to choose between the streaming and the tiled kernel.
+// fmt: weight format (Fmt in moe_common.hpp; the token side is MX-fp8 for
+// FMT_MX4 and the same format otherwise); out_fmt: FMT_F32, FMT_BF16, or for
+// SwiGLU FMT_MX8 (MX formats) / FMT_FP8 (static FP8).  total_rows: rows of
+// all segments, used only to choose between the streaming and the tiled
+// kernel.
 hipError_t launch_grouped_gemm(const GemmArgs &g, int fmt, int epi, int out_fmt, int total_rows,
                                hipStream_t stream);
 
