@@ -90,12 +90,23 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT *__restrict
   }
 }
 
+// Batches of at most this many tokens: the router GEMM splits the fp32
+// weights itself, stage by stage, instead of reading a copy split once per
+// call by router_split_kernel.  Both give the same bits.  Measured on the
+// Hy3 shape: decode (T = 64) gating 24.2 -> 20.8 us; at T = 8192 the split
+// repeated by every token tile costs more than the separate pass (95 ->
+// 116 us), so large batches keep it.
+#ifndef MOE_ROUTER_FUSED_SPLIT_T
+#define MOE_ROUTER_FUSED_SPLIT_T 256
+#endif
+
 // bf16 activations: matrix-core kernels.  W_r is split exactly into three
 // bf16 terms, w = hi + mid + lo (each remainder is exact in fp32 and the last
 // holds at most 8 significant bits), so x . w = x . hi + x . mid + x . lo
 // with every product exact in fp32; three bf16 MFMAs per step accumulate the
-// sum in fp32.  The split is done once per call by router_split_kernel into
-// fragment order; router_gemm_kernel then only loads and multiplies.
+// sum in fp32.  For large batches the split is done once per call by
+// router_split_kernel into fragment order, and router_gemm_kernel only loads
+// and multiplies; for small ones the GEMM splits the fp32 rows it loads.
 //
 // Fragment layout as in moe_common.hpp: W_r rows are the A operand (lane
 // row = expert), x rows the B operand (lane column = token).  A stage is 64
@@ -164,9 +175,10 @@ __global__ __launch_bounds__(256) void router_split_kernel(const float *__restri
 // grid is dealt round-robin to the 8 XCDs and each XCD takes one contiguous
 // range of that order, so an XCD's L2 holds the split weights of one or two
 // K slices while the expert tiles that share a token tile run side by side.
-template <int MBT, int WPF>
+template <int MBT, int WPF, bool FS>
 __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__restrict__ x,
                                                           const uint4 *__restrict__ wsplit,
+                                                          const float *__restrict__ Wr,
                                                           float *__restrict__ part, int T, int H,
                                                           int E, int EB, int nsl, int n_et,
                                                           int n_tt, int ksn) {
@@ -209,18 +221,55 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
 #pragma unroll
     for (int i = 0; i < TLD; ++i) *(i32x4 *)(buf + tdst[i]) = treg[i];
   };
-  // weight fragments of one stage: [term][pp]
+  // FS: fp32 weights of one stage, [pp][2 x 4 elements], split into the
+  // three bf16 terms when the stage multiplies them.  Otherwise the split
+  // fragments of one stage, [term][pp].
+  const int we = 16 * eb + (lane & 15);
+  const bool we_ok = we < E;
+  const float *wrow = Wr + (size_t)min(we, E - 1) * H + 8 * (lane >> 4);
+  f32x4 wf[NSET][2][2];
   i32x4 wr[NSET][3][2];
   auto load_weights = [&](int s, int set) MOE_INLINE {
+    if constexpr (FS) {
 #pragma unroll
-    for (int term = 0; term < 3; ++term)
+      for (int pp = 0; pp < 2; ++pp)
 #pragma unroll
-      for (int pp = 0; pp < 2; ++pp) {
-        const uint4 v = wbase[term * per_term + (long long)s * 128 + pp * 64];
+        for (int h = 0; h < 2; ++h) {
+          const f32x4 v = *(const f32x4 *)(wrow + 64 * s + 32 * pp + 4 * h);
 #pragma unroll
-        for (int q = 0; q < NSET; ++q)
-          if (q == set) wr[q][term][pp] = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+          for (int q = 0; q < NSET; ++q)
+            if (q == set) wf[q][pp][h] = v;
+        }
+    } else {
+#pragma unroll
+      for (int term = 0; term < 3; ++term)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const uint4 v = wbase[term * per_term + (long long)s * 128 + pp * 64];
+#pragma unroll
+          for (int q = 0; q < NSET; ++q)
+            if (q == set) wr[q][term][pp] = i32x4{(int)v.x, (int)v.y, (int)v.z, (int)v.w};
+        }
+    }
+  };
+  auto split_weights = [&](int set, i32x4 (&w)[3][2]) MOE_INLINE {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[j] = we_ok ? wf[set][pp][0][j] : 0.0f;
+        v[4 + j] = we_ok ? wf[set][pp][1][j] : 0.0f;
       }
+      uint16_t t[3][8];
+      split_bf16x3(v, t[0], t[1], t[2]);
+#pragma unroll
+      for (int term = 0; term < 3; ++term)
+        w[term][pp] = i32x4{(int)((uint32_t)t[term][0] | ((uint32_t)t[term][1] << 16)),
+                            (int)((uint32_t)t[term][2] | ((uint32_t)t[term][3] << 16)),
+                            (int)((uint32_t)t[term][4] | ((uint32_t)t[term][5] << 16)),
+                            (int)((uint32_t)t[term][6] | ((uint32_t)t[term][7] << 16))};
+    }
   };
   f32x4 acc[MBT];
 #pragma unroll
@@ -231,6 +280,15 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
     constexpr int set = decltype(set_c)::value, slot = decltype(slot_c)::value;
     load_weights(min(s + WPF, s_end - 1), (set + WPF) % NSET);
     const uint8_t *base = slot ? tb1 : tb0;
+    i32x4 ws[3][2];
+    if constexpr (FS) {
+      split_weights(set, ws);
+    } else {
+#pragma unroll
+      for (int term = 0; term < 3; ++term)
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) ws[term][pp] = wr[set][term][pp];
+    }
 #pragma unroll
     for (int m = 0; m < MBT; ++m) {
       const uint8_t *p = base + m * 2048;
@@ -239,11 +297,11 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
 #pragma unroll
       for (int term = 0; term < 3; ++term) {
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, wr[set][term][0]), __builtin_bit_cast(bf16x8, b0), acc[m],
-            0, 0, 0);
+            __builtin_bit_cast(bf16x8, ws[term][0]), __builtin_bit_cast(bf16x8, b0), acc[m], 0,
+            0, 0);
         acc[m] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-            __builtin_bit_cast(bf16x8, wr[set][term][1]), __builtin_bit_cast(bf16x8, b1), acc[m],
-            0, 0, 0);
+            __builtin_bit_cast(bf16x8, ws[term][1]), __builtin_bit_cast(bf16x8, b1), acc[m], 0,
+            0, 0);
       }
     }
     store_tokens(slot ? tb0 : tb1);
@@ -412,16 +470,24 @@ hipError_t launch_route(const void *x, int x_is_bf16, const float *Wr, const flo
   const RoutePlan p = router_plan(T, H, E, x_is_bf16);
   const int ksn = p.ksn;
   if (x_is_bf16) {
+    const bool fused = T <= MOE_ROUTER_FUSED_SPLIT_T;
     const size_t pbytes = (((size_t)ksn * T * E * sizeof(float)) + 255) & ~(size_t)255;
     uint4 *wsplit = (uint4 *)((char *)part + pbytes);
-    const long long nthr = (long long)p.eb * (H / 64) * 128;
-    router_split_kernel<<<(unsigned)((nthr + 255) / 256), blk, 0, stream>>>(Wr, E, H, p.eb, wsplit);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
+    if (!fused) {
+      const long long nthr = (long long)p.eb * (H / 64) * 128;
+      router_split_kernel<<<(unsigned)((nthr + 255) / 256), blk, 0, stream>>>(Wr, E, H, p.eb,
+                                                                               wsplit);
+      hipError_t err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
     const int n_et = (p.eb + 3) / 4, n_tt = (T + 16 * p.mbt - 1) / (16 * p.mbt);
     const int per_xcd = (n_et * n_tt * ksn + 7) / 8;
-    router_gemm_kernel<4, 2><<<per_xcd * 8, blk, 0, stream>>>((const uint16_t *)x, wsplit, part, T,
-                                                               H, E, p.eb, p.nsl, n_et, n_tt, ksn);
+    if (fused)
+      router_gemm_kernel<4, 2, true><<<per_xcd * 8, blk, 0, stream>>>(
+          (const uint16_t *)x, wsplit, Wr, part, T, H, E, p.eb, p.nsl, n_et, n_tt, ksn);
+    else
+      router_gemm_kernel<4, 2, false><<<per_xcd * 8, blk, 0, stream>>>(
+          (const uint16_t *)x, wsplit, Wr, part, T, H, E, p.eb, p.nsl, n_et, n_tt, ksn);
   } else {
     if (T <= 256) {
       dim3 grid((T + 15) / 16, (E + 63) / 64);
