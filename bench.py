@@ -86,7 +86,7 @@ def measured_traffic(workload: str):
 def main():
     a = parse()
     if a.gpus != 1:
-        print("bench.py measures one GPU: this build runs the whole MoE layer on a single "
+        print("bench.py measures one GPU: the library runs the whole MoE layer on a single "
               "MI355X and has no multi-GPU path (--gpus %d requested)" % a.gpus, file=sys.stderr)
         sys.exit(2)
 

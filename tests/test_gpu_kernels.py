@@ -211,7 +211,7 @@ def test_route_parity(orc, ctx, name, T):
     ok = ~mism
     rel = np.abs(g_w[ok].astype(np.float64) - o_w[ok]) / np.abs(o_w[ok])
     assert rel.max() <= 1e-6, rel.max()
-    # BASELINE check: routed weights sum to the scaling factor
+    # the routed weights of a token sum to the scaling factor
     assert np.abs(g_w.astype(np.float64).sum(1) - 2.826).max() <= 1e-5
 
 

@@ -135,7 +135,7 @@ def test_layer_equals_per_token_definition(orc):
             ref[t] += float(w[t, j]) * dense_swiglu(x[t:t + 1], Wg[e], Wu[e], Wd[e])[0]
         ref[t] += sh[t]
     assert rel_err(r["out"], ref) < 1e-6
-    # BASELINE check: tokens per expert sum to T*k
+    # the pairs routed to all experts number T*k
     assert r["counts"].sum() == 64 * 4
 
 
