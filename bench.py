@@ -12,6 +12,9 @@ prefill batch, reported under "prefill".  Prints one JSON line.
                launch over its mean duration from HIP events recorded around
                it on its own stream during profiled steps
   cpu_baseline the CPU oracle on a bounded sample of the same batch
+  parity       that sample's oracle output against the timed batch's: routing
+               index mismatches (and tie flips among them) and the largest
+               relative output error
 """
 from __future__ import annotations
 
@@ -178,7 +181,11 @@ def main():
     xd = to_device(xg, dev)
     T = w.T
     log("timing %s: T=%d, %d warm-up + %d steps" % (w.name, T, a.warmup, a.steps))
-    ms, wall_ms, _ = run(xd, T, a.steps, a.warmup)
+    ms, wall_ms, out_decode = run(xd, T, a.steps, a.warmup)
+    out_host = out_decode.float().cpu().numpy()
+    ws = lay.workspace(T)
+    io, _ = B.moe_layer_ws_topk(lay.desc, T)
+    idx_host = ws[io:io + 4 * T * w.k].view(torch.int32).reshape(T, w.k).cpu().numpy()
     touched = routed_experts(T)
     stages = stage_profile(xd, T, a.profile_steps)
     P = T * w.k
@@ -276,7 +283,7 @@ def main():
         oracle.build(force=False)
 
         def oracle_tokens(toks):
-            oracle.layer_forward_tokens(toks, x32, Wr, bias, lambda e: (Wg[e], Wu[e], Wd[e]),
+            return oracle.layer_forward_tokens(toks, x32, Wr, bias, lambda e: (Wg[e], Wu[e], Wd[e]),
                                         shared, k=w.k, rho=w.rho, route_norm=w.route_norm,
                                         mx={"mxfp8": 1, "w4a8": 2}.get(w.dtype, 0),
                                         fp8=((w.fp8_x_scale, w.fp8_h_scale, w.fp8_sh_h_scale)
@@ -296,6 +303,20 @@ def main():
         for _ in range(reps):
             oracle_tokens(np.arange(n))
         dt = time.perf_counter() - t1
+        # parity of the timed batch on the same sample: routing indices
+        # (mismatches, and those inside the oracle's 1e-6 score gap at the
+        # top-k boundary, i.e. tie flips) and the output relative to the
+        # largest oracle magnitude, over the tokens whose routing agrees
+        ref, o_idx, _, gap = oracle_tokens(np.arange(n))
+        mism = (idx_host[:n] != o_idx).any(axis=1)
+        keep = ~mism
+        err = (float(np.abs(out_host[:n][keep].astype(np.float64) - ref[keep]).max()
+                     / np.abs(ref[keep]).max()) if keep.any() else None)
+        result["parity"] = {
+            "tokens": n, "index_mismatches": int(mism.sum()),
+            "tie_flips": int((mism & (gap <= 1e-6)).sum()),
+            "max_rel_err": None if err is None else float("%.3g" % err),
+            "tolerance": {"f32": 1e-5, "bf16": 1e-2}.get(w.dtype, 3e-2)}
         result["cpu_baseline"] = {
             "value": round(n * reps / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
             "kind": "oracle",
