@@ -26,6 +26,37 @@ __device__ __forceinline__ float load_src(const void *p, long long i) {
   else return ((const float *)p)[i];
 }
 
+// v[0..N) = src[i0, i0 + N) widened to fp32; VEC: with 16-byte loads (the
+// address of element i0 is 16-byte aligned), else one element at a time.
+template <bool BF16, bool VEC, int N>
+__device__ __forceinline__ void load_run(const void *src, long long i0, float (&v)[N]) {
+  if constexpr (VEC && BF16) {
+    static_assert(N % 8 == 0, "whole 16-byte vectors");
+    const uint4 *p = (const uint4 *)((const uint16_t *)src + i0);
+#pragma unroll
+    for (int q = 0; q < N / 8; ++q) {
+      const uint4 u = p[q];
+      const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[8 * q + 2 * j] = __uint_as_float(w[j] << 16);
+        v[8 * q + 2 * j + 1] = __uint_as_float(w[j] & 0xFFFF0000u);
+      }
+    }
+  } else if constexpr (VEC) {
+    static_assert(N % 4 == 0, "whole 16-byte vectors");
+    const float4 *p = (const float4 *)((const float *)src + i0);
+#pragma unroll
+    for (int q = 0; q < N / 4; ++q) {
+      const float4 a = p[q];
+      v[4 * q] = a.x; v[4 * q + 1] = a.y; v[4 * q + 2] = a.z; v[4 * q + 3] = a.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) v[i] = load_src<BF16>(src, i0 + i);
+  }
+}
+
 // Quantise 32 values v[0..31] (registers) to codes and scale byte.
 __device__ __forceinline__ void mx_block(const float (&v)[32], uint32_t (&codes)[8], uint32_t &sb) {
   float am = 0.0f;
@@ -62,7 +93,7 @@ __device__ __forceinline__ void mx4_block(const float (&v)[32], uint32_t (&codes
 
 // ----------------------------------------------------------------------------- activations
 // One thread per 32-element block of a row-major [rows, cols] matrix.
-template <bool BF16>
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void mx_quantize_kernel(const void *__restrict__ src,
                                                           long long rows, long long cols,
                                                           uint8_t *__restrict__ q,
@@ -71,8 +102,7 @@ __global__ __launch_bounds__(256) void mx_quantize_kernel(const void *__restrict
   const long long b = (long long)blockIdx.x * 256 + threadIdx.x;
   if (b >= nblk) return;
   float v[32];
-#pragma unroll
-  for (int i = 0; i < 32; ++i) v[i] = load_src<BF16>(src, b * 32 + i);
+  load_run<BF16, VEC>(src, b * 32, v);
   uint32_t codes[8], sb;
   mx_block(v, codes, sb);
   uint4 *o = (uint4 *)(q + b * 32);
@@ -86,10 +116,16 @@ hipError_t launch_mx_quantize(const void *src, int src_is_bf16, long long rows, 
   const long long nblk = rows * (cols / 32);
   if (nblk <= 0) return hipSuccess;
   const unsigned grid = (unsigned)((nblk + 255) / 256);
-  if (src_is_bf16)
-    mx_quantize_kernel<true><<<grid, 256, 0, stream>>>(src, rows, cols, q, scale);
+  // every 32-element block starts 16-byte aligned when the array does
+  const bool vec = ((uintptr_t)src & 15) == 0;
+  if (src_is_bf16 && vec)
+    mx_quantize_kernel<true, true><<<grid, 256, 0, stream>>>(src, rows, cols, q, scale);
+  else if (src_is_bf16)
+    mx_quantize_kernel<true, false><<<grid, 256, 0, stream>>>(src, rows, cols, q, scale);
+  else if (vec)
+    mx_quantize_kernel<false, true><<<grid, 256, 0, stream>>>(src, rows, cols, q, scale);
   else
-    mx_quantize_kernel<false><<<grid, 256, 0, stream>>>(src, rows, cols, q, scale);
+    mx_quantize_kernel<false, false><<<grid, 256, 0, stream>>>(src, rows, cols, q, scale);
   return hipGetLastError();
 }
 
@@ -98,15 +134,17 @@ hipError_t launch_mx_quantize(const void *src, int src_is_bf16, long long rows, 
 // families): one fp32 scale per weight tensor, max|w| / 448, and fixed
 // activation scales; codes are E4M3 of fp32(v / scale).
 // E4M3 codes of fp32(src / scale): one thread per 8 elements (n % 8 == 0).
-template <bool BF16>
+template <bool BF16, bool VEC>
 __global__ __launch_bounds__(256) void fp8_quantize_kernel(const void *__restrict__ src,
                                                            long long n8, float scale,
                                                            uint8_t *__restrict__ q) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
   if (i >= n8) return;
+  float v[8];
+  load_run<BF16, VEC>(src, 8 * i, v);
   uint32_t c[2] = {0u, 0u};
 #pragma unroll
-  for (int j = 0; j < 8; ++j) c[j >> 2] |= e4m3_rne(load_src<BF16>(src, 8 * i + j) / scale) << (8 * (j & 3));
+  for (int j = 0; j < 8; ++j) c[j >> 2] |= e4m3_rne(v[j] / scale) << (8 * (j & 3));
   *(uint2 *)(q + 8 * i) = make_uint2(c[0], c[1]);
 }
 
@@ -116,10 +154,16 @@ hipError_t launch_fp8_quantize(const void *src, int src_is_bf16, long long n, fl
   if (n % 8) return hipErrorInvalidValue;
   const long long n8 = n / 8;
   const unsigned grid = (unsigned)((n8 + 255) / 256);
-  if (src_is_bf16)
-    fp8_quantize_kernel<true><<<grid, 256, 0, stream>>>(src, n8, scale, q);
+  // runs of 8 elements start 16-byte aligned when the array does
+  const bool vec = ((uintptr_t)src & 15) == 0;
+  if (src_is_bf16 && vec)
+    fp8_quantize_kernel<true, true><<<grid, 256, 0, stream>>>(src, n8, scale, q);
+  else if (src_is_bf16)
+    fp8_quantize_kernel<true, false><<<grid, 256, 0, stream>>>(src, n8, scale, q);
+  else if (vec)
+    fp8_quantize_kernel<false, true><<<grid, 256, 0, stream>>>(src, n8, scale, q);
   else
-    fp8_quantize_kernel<false><<<grid, 256, 0, stream>>>(src, n8, scale, q);
+    fp8_quantize_kernel<false, false><<<grid, 256, 0, stream>>>(src, n8, scale, q);
   return hipGetLastError();
 }
 

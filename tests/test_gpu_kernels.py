@@ -34,7 +34,8 @@ def dev(a):
 
 
 @pytest.mark.parametrize("src", ["f32", "bf16"])
-def test_mx_quantize_bit_exact(orc, src):
+@pytest.mark.parametrize("offset", [0, 2])
+def test_mx_quantize_bit_exact(orc, src, offset):
     rng = np.random.default_rng(1)
     rows, cols = 67, 512
     v = (rng.standard_normal((rows, cols)) * np.exp(rng.uniform(-12, 12, (rows, 1)))).astype(np.float32)
@@ -49,6 +50,11 @@ def test_mx_quantize_bit_exact(orc, src):
     else:
         xin, ref = dev(v), v
         dt = B.MOE_F32
+    if offset:
+        # the same values at an address that is not 16-byte aligned
+        buf = torch.zeros(xin.numel() + offset, dtype=xin.dtype, device="cuda")
+        buf[offset:] = xin.reshape(-1)
+        xin = buf[offset:]
     q = torch.empty((rows, cols), dtype=torch.uint8, device="cuda")
     s = torch.empty((rows, cols // 32), dtype=torch.uint8, device="cuda")
     B.moe_mx_quantize(xin, dt, rows, cols, q, s)
@@ -59,7 +65,8 @@ def test_mx_quantize_bit_exact(orc, src):
 
 
 @pytest.mark.parametrize("src", ["f32", "bf16"])
-def test_fp8_quantize_bit_exact(orc, src):
+@pytest.mark.parametrize("offset", [0, 2])
+def test_fp8_quantize_bit_exact(orc, src, offset):
     rng = np.random.default_rng(6)
     n, s = 8 * 4099, 2.0 ** -5
     v = (rng.standard_normal(n) * np.exp(rng.uniform(-9, 3, n))).astype(np.float32)
@@ -69,6 +76,11 @@ def test_fp8_quantize_bit_exact(orc, src):
         xin, ref, dt = dev(bits), I.bf16_widen(bits), B.MOE_BF16
     else:
         xin, ref, dt = dev(v), v, B.MOE_F32
+    if offset:
+        # the same values at an address that is not 16-byte aligned
+        buf = torch.zeros(xin.numel() + offset, dtype=xin.dtype, device="cuda")
+        buf[offset:] = xin
+        xin = buf[offset:]
     for scale in (s, 0.0123):
         q = torch.empty(n, dtype=torch.uint8, device="cuda")
         B.moe_fp8_quantize(xin, dt, n, scale, q)
