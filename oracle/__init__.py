@@ -79,6 +79,7 @@ def _load():
         lib.oracle_router_logits.argtypes = [I64, I64, I64, P, P, P, P]
         lib.oracle_route.argtypes = [I64, I64, I64, I64, P, P, P, ctypes.c_float, ctypes.c_int,
                                      P, P, P, P]
+        lib.oracle_route_weights.argtypes = [I64, I64, I64, P, P, ctypes.c_float, ctypes.c_int, P]
         lib.oracle_permute.argtypes = [I64, I64, I64, P, P, P, P, P]
         lib.oracle_swiglu_rows.argtypes = [I64, I64, I64, P, ctypes.c_int, P, P, P, ctypes.c_int,
                                            P, P]
@@ -88,7 +89,7 @@ def _load():
             + [P] * 6 + [ctypes.c_int] + [P] * 10)
         for name in ("oracle_mxq", "oracle_mx_dequant", "oracle_mxq4", "oracle_mx4_dequant",
                      "oracle_fp8_quantize", "oracle_swiglu_rows_fp8",
-                     "oracle_router_logits", "oracle_route",
+                     "oracle_router_logits", "oracle_route", "oracle_route_weights",
                      "oracle_permute", "oracle_swiglu_rows", "oracle_combine",
                      "oracle_layer_forward"):
             getattr(lib, name).restype = ctypes.c_int
@@ -263,6 +264,22 @@ def route(x, Wr, bias, k, rho, route_norm=True):
     return idx, w, s, gap
 
 
+def route_weights(scores, topk_idx, rho, route_norm=True):
+    """Gating step 4 on a given selection: topk_w [T,k] from this oracle's
+    sigmoid scores [T,E] and the selected experts topk_idx [T,k] (k distinct
+    experts per row)."""
+    s = _f32(scores)
+    idx = _i32(topk_idx)
+    T, E = s.shape
+    k = idx.shape[1]
+    if idx.shape[0] != T:
+        raise ValueError("scores and topk_idx disagree on T")
+    w = np.empty((T, k), np.float32)
+    _check(_load().oracle_route_weights(T, E, k, _p(s), _p(idx), ctypes.c_float(rho),
+                                        int(bool(route_norm)), _p(w)), "route_weights")
+    return w
+
+
 def permute(topk_idx, E):
     """InitRouting.  Returns (counts [E], offsets [E+1], sorted_src [T*k], dest [T*k])."""
     idx = _i32(topk_idx)
@@ -342,17 +359,24 @@ def layer_forward(x, Wr, bias, Wg, Wu, Wd, Sg=None, Su=None, Sd=None, *, k, rho,
 
 
 def layer_forward_tokens(tokens, x, Wr, bias, expert_weights, shared_weights, *, k, rho,
-                         route_norm=True, mx=False, fp8=None):
+                         route_norm=True, mx=False, fp8=None, topk_idx=None):
     """Layer output for selected tokens only, straight from the definition.
 
     ``expert_weights(e)`` returns (Wg [I,H], Wu [I,H], Wd [H,I]) of expert e;
     ``shared_weights`` is (Sg, Su, Sd) or None.  ``fp8`` = (s_x, s_h, s_h_shared)
     selects static per-tensor FP8 experts (fp32 masters in, quantised here)
-    with those activation scales; otherwise ``mx`` applies.  Returns (out [n,H],
-    topk_idx [n,k], topk_w [n,k], gap [n]) for ``x[tokens]``."""
+    with those activation scales; otherwise ``mx`` applies.  ``topk_idx``
+    ([n,k], optional) replaces this oracle's selection for these tokens by a
+    given one (whose weights then follow step 4 from this oracle's scores):
+    how a token whose selection differs only by near-equal scores is
+    evaluated.  Returns (out [n,H], topk_idx [n,k], topk_w [n,k], gap [n])
+    for ``x[tokens]``."""
     tokens = np.asarray(tokens, dtype=np.int64)
     xs = _f32(np.asarray(x)[tokens])
-    idx, w, _, gap = route(xs, Wr, bias, k, rho, route_norm)
+    idx, w, scores, gap = route(xs, Wr, bias, k, rho, route_norm)
+    if topk_idx is not None:
+        idx = _i32(topk_idx).reshape(len(tokens), k)
+        w = route_weights(scores, idx, rho, route_norm)
     n, H = xs.shape
     out = np.empty((n, H), np.float32)
     # Evaluate each needed expert once over the tokens that picked it.

@@ -269,6 +269,43 @@ static int ranks_before(float sa, int a, float sb, int b) {
   return a < b;
 }
 
+/* Step 4 for one token: w[j] = fp32( rho * s[idx_j] / sum_j s[idx_j] ) with
+ * the denominator summed in double over j ascending (route_norm = 1), or
+ * fp32( rho * s[idx_j] ) (route_norm = 0).  route_norm and
+ * router_scaling_factor: Hy3 guide, section 1. */
+static void route_weights_row(int64_t k, const float *s, const int32_t *idx, float rho,
+                              int route_norm, float *w) {
+  double den = 0.0;
+  for (int64_t j = 0; j < k; ++j) den += (double)s[idx[j]];
+  for (int64_t j = 0; j < k; ++j) {
+    double sj = (double)s[idx[j]];
+    double wj = route_norm ? (double)rho * sj / den : (double)rho * sj;
+    w[j] = (float)wj;
+  }
+}
+
+/* Step 4 on selections given from outside (a selection another gating
+ * produced, e.g. one that differs from this oracle's only by near-equal
+ * scores): scores [T,E] are this oracle's sigmoid scores, idx [T,k] the
+ * selected experts.  Returns -1 unless every row holds k distinct experts
+ * in [0, E). */
+ORC_EXPORT int oracle_route_weights(int64_t T, int64_t E, int64_t k, const float *scores,
+                                    const int32_t *idx, float rho, int route_norm, float *w) {
+  if (T < 0 || E <= 0 || k <= 0 || k > E) return -1;
+  if (T == 0) return 0;
+  if (!scores || !idx || !w) return -1;
+  for (int64_t t = 0; t < T; ++t)
+    for (int64_t j = 0; j < k; ++j) {
+      int32_t e = idx[t * k + j];
+      if (e < 0 || e >= E) return -1;
+      for (int64_t i = 0; i < j; ++i)
+        if (idx[t * k + i] == e) return -1;
+    }
+  for (int64_t t = 0; t < T; ++t)
+    route_weights_row(k, scores + t * E, idx + t * k, rho, route_norm, w + t * k);
+  return 0;
+}
+
 /* Full gating for T tokens.
  *   topk_idx [T,k] int32 : selected experts, best first
  *   topk_w   [T,k] fp32  : rho * s / sum(selected s)   (route_norm = 1)
@@ -323,13 +360,7 @@ ORC_EXPORT int oracle_route(int64_t T, int64_t H, int64_t E, int64_t k, const fl
             gap[t] = s[topk_idx[t * k + k - 1]] - s[next];
           }
         }
-        double den = 0.0;
-        for (int64_t j = 0; j < k; ++j) den += (double)s[topk_idx[t * k + j]];
-        for (int64_t j = 0; j < k; ++j) {
-          double sj = (double)s[topk_idx[t * k + j]];
-          double wj = route_norm ? (double)rho * sj / den : (double)rho * sj;
-          topk_w[t * k + j] = (float)wj;
-        }
+        route_weights_row(k, s, topk_idx + t * k, rho, route_norm, topk_w + t * k);
       }
     }
     free(s);

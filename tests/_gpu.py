@@ -7,8 +7,8 @@ from concurrent.futures import ThreadPoolExecutor
 import numpy as np
 
 from mixture_experts_layer_19_amd import inputs as I
+from oracle.parity import classify_routing
 
-TIE_MARGIN = 1e-6          # sigmoid-score margin inside which a routing flip is a tie
 TOL = {"f32": 1e-5, "bf16": 1e-2, "mxfp8": 3e-2, "w4a8": 3e-2, "fp8": 3e-2}
 
 _layers = {}
@@ -47,20 +47,46 @@ def rel_max_err(gpu, ref):
     return float(np.abs(gpu - ref).max() / np.abs(ref).max())
 
 
-def classify_routing(g_idx, o_idx, scores):
-    """Rows where the GPU's indices differ from the oracle's.  A row is a tie
-    flip when, slot by slot, the oracle's scores of the two experts differ by
-    at most TIE_MARGIN (a swap at the top-k boundary or inside the selection
-    among near-equal scores).  Returns (mismatch mask, tie-flip mask)."""
-    mism = (g_idx != o_idx).any(axis=1)
-    flips = np.zeros_like(mism)
-    for t in np.nonzero(mism)[0]:
-        sg = scores[t, g_idx[t]].astype(np.float64)
-        so = scores[t, o_idx[t]].astype(np.float64)
-        distinct = len(set(g_idx[t].tolist())) == len(g_idx[t])
-        in_range = np.all((g_idx[t] >= 0) & (g_idx[t] < scores.shape[1]))
-        flips[t] = distinct and in_range and np.all(np.abs(sg - so) <= TIE_MARGIN)
-    return mism, flips
+# per-workload parity margins of this session, printed by conftest's summary
+MARGINS = []
+
+
+def compare_layer(orc, w: I.Workload, x, out, g_idx, toks, label=None):
+    """Compare the GPU layer output ``out`` [T,H] for tokens ``toks`` with the
+    oracle.  The GPU's routing ``g_idx`` [T,k] must equal the oracle's except
+    on tie flips (oracle.parity's rule); a flipped token is evaluated by the
+    oracle with the GPU's selection, so every token in ``toks`` is compared.
+    Returns the relative error max|gpu - oracle| / max|oracle| and records
+    it with the token and flip counts in MARGINS."""
+    Wr, b = I.router_weight(w), I.router_bias(w)
+    o_idx, _, scores, _ = orc.route(x, Wr, b, w.k, w.rho, w.route_norm)
+    mism, flips = classify_routing(g_idx, o_idx, scores)
+    bad = np.nonzero(mism & ~flips)[0]
+    assert len(bad) == 0, "routing differs beyond near-ties at tokens %s" % bad[:10].tolist()
+    toks = np.asarray(toks)
+    flipped = toks[flips[toks]]
+    plain = toks[~flips[toks]]
+    experts = np.concatenate([o_idx[plain].ravel(), g_idx[flipped].ravel()])
+    ew = expert_weights_parallel(w, experts)
+    kw = dict(k=w.k, rho=w.rho, route_norm=w.route_norm, mx=oracle_mx(w.dtype), fp8=oracle_fp8(w))
+    shared = I.shared_stored(w) if w.Is else None
+    ref = np.empty((len(toks), w.H), np.float32)
+    where = {int(t): i for i, t in enumerate(toks)}
+    if len(plain):
+        r, idx, _, _ = orc.layer_forward_tokens(plain, x, Wr, b, lambda e: ew[e], shared, **kw)
+        np.testing.assert_array_equal(idx, o_idx[plain])
+        ref[[where[int(t)] for t in plain]] = r
+    if len(flipped):
+        r, _, _, _ = orc.layer_forward_tokens(flipped, x, Wr, b, lambda e: ew[e], shared,
+                                              topk_idx=g_idx[flipped], **kw)
+        ref[[where[int(t)] for t in flipped]] = r
+    err = rel_max_err(out[toks], ref)
+    MARGINS.append(dict(workload=label or w.name, T=w.T, compared=len(toks),
+                        tie_flips=int(flips.sum()), flips_compared=len(flipped),
+                        rel_err=err, tol=TOL[w.dtype]))
+    print("[layer] %s T=%d: %d of %d tokens compared (%d tie flips, all re-evaluated), rel err %.3g"
+          % (label or w.name, w.T, len(toks), w.T, int(flips.sum()), err), flush=True)
+    return err
 
 
 def expert_weights_parallel(w: I.Workload, experts, threads=None):

@@ -18,3 +18,17 @@ def orc():
     import oracle
     oracle.build(force=False)
     return oracle
+
+
+def pytest_terminal_summary(terminalreporter):
+    """Per-workload parity margins of the GPU layer tests (if any ran)."""
+    mod = sys.modules.get("_gpu")
+    rows = getattr(mod, "MARGINS", None) if mod else None
+    if not rows:
+        return
+    tr = terminalreporter
+    tr.write_sep("-", "layer parity margins (max|gpu-oracle|/max|oracle|, every token)")
+    for r in rows:
+        tr.write_line("%-28s T=%-5d tokens %-5d tie flips %-3d rel err %.3g (tol %g)"
+                      % (r["workload"], r["T"], r["compared"], r["tie_flips"], r["rel_err"],
+                         r["tol"]))
