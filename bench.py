@@ -3,18 +3,26 @@
 A step is one moe_layer_forward call (gating, permutation, routed grouped
 SwiGLU GEMM, shared expert on the side stream, combine) over one batch of
 synthetic tokens, with weights and inputs already resident in HBM.  The
-default workload is the Hy3-shape decode batch (T = 64, H = 4096, 192
-experts, top-8, I = I_s = 1536, bf16); the same weights then run the T = 8192
-prefill batch, reported under "prefill".  Prints one JSON line.
+default run times the five workloads (tiny fp32, Hy3 decode T = 64, Hy3
+prefill T = 8192, Hy4-shape skewed T = 2048, MX-fp8 T = 4096) and prints one
+JSON line whose headline is the Hy3 decode batch; every workload has its own
+object under "workloads".
 
-  roofline     dominant kernel (the routed gate/up + SwiGLU GEMM): algorithmic
-               bytes (decode, HBM-bound) or flops (prefill, MFMA-bound) per
-               launch over its mean duration from HIP events recorded around
-               it on its own stream during profiled steps
-  cpu_baseline the CPU oracle on a bounded sample of the same batch
-  parity       that sample's oracle output against the timed batch's: routing
-               index mismatches (and tie flips among them) and the largest
-               relative output error
+Timing: each timed step is bracketed by HIP events on the caller's stream;
+before every step (outside the bracket) a 1 GiB fill evicts L2 and the
+256 MB MALL.  Reported: the median step, with p10 and p90.
+
+  roofline     the dominant kernel (the routed gate/up + SwiGLU GEMM): its
+               algorithmic bytes (HBM-bound workloads) or flops (prefill) per
+               launch over its duration, timed with HIP events recorded
+               around it on its own stream (median of profiled steps)
+  layer        the whole step against HBM and matrix-core peaks
+  parity       the oracle on a sample of the timed batch's tokens against the
+               GPU output: routing mismatches, tie flips (evaluated with the
+               GPU's selection), largest relative error
+  cpu_baseline the CPU oracle on a bounded sample of the headline batch
+
+``--trace-summary DIR`` instead summarises a rocprofv3 kernel trace (no GPU).
 """
 from __future__ import annotations
 
@@ -31,34 +39,57 @@ if ROOT not in sys.path:
 METRIC = "MoE-layer tokens/s + %HBM (T=64) / %MFMA peak (T=8192), Hy3 shape, 1 GPU"
 HBM_PEAK_GBPS = 8000.0           # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2516.6        # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 flop/clk)
-FP8_PEAK_TFLOPS = 5033.2
+FP8_PEAK_TFLOPS = 5033.2         # dense fp8 / MX-fp8
+FP32_PEAK_TFLOPS = 157.3         # fp32 matrix / vector
+DEFAULT_WORKLOADS = ["hy3_decode", "tiny", "hy3_prefill", "hy4_skew", "mx"]
+# workloads whose binding roofline is the matrix cores (the others: HBM)
+MFMA_BOUND = {"hy3_prefill"}
 
 
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="hy3_decode",
-                    choices=["hy3_decode", "hy3_prefill", "hy4_skew", "mx", "tiny", "w4a8_decode",
-                             "w4a8", "fp8_decode", "fp8"])
-    ap.add_argument("--profile-steps", type=int, default=20)
-    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="all",
+                    choices=["all", "hy3_decode", "hy3_prefill", "hy4_skew", "mx", "tiny",
+                             "w4a8_decode", "w4a8", "fp8_decode", "fp8"])
+    ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the batch replayed from a captured HIP graph")
+    ap.add_argument("--no-flush", action="store_true",
+                    help="do not evict the caches before each timed step")
     ap.add_argument("--single-stream", action="store_true",
                     help="run the shared expert on the main stream (per-stage times then "
                          "measure each kernel alone)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
+    ap.add_argument("--trace-summary", metavar="DIR",
+                    help="summarise the rocprofv3 kernel trace under DIR and exit")
     return ap.parse_args()
 
 
 def log(msg):
     print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def pct(v, q):
+    import numpy as np
+    return float(np.percentile(np.asarray(v, dtype=np.float64), q))
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def measured_traffic(workload: str):
@@ -79,6 +110,7 @@ def measured_traffic(workload: str):
         kv[k.strip()] = v.strip()
     h = hashlib.sha256()
     for f in ("mixture_experts_layer_19_amd/csrc/gemm.hip",
+              "mixture_experts_layer_19_amd/csrc/gemm_common.hpp",
               "mixture_experts_layer_19_amd/csrc/moe_common.hpp"):
         h.update(open(os.path.join(ROOT, f), "rb").read())
     if kv.get("source_sha256") != h.hexdigest():
@@ -86,8 +118,69 @@ def measured_traffic(workload: str):
     return int(kv["traffic_bytes"])
 
 
+# ----------------------------------------------------------------------------- trace summary
+
+
+def trace_summary(d: str) -> None:
+    """Per-kernel statistics of a rocprofv3 kernel trace, with the routed and
+    the shared-expert launches (the latter on the side stream) in separate
+    rows, and the overlap of the shared expert with the main stream."""
+    import csv
+    import glob
+    import re
+    files = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        sys.exit("no *kernel_trace.csv under %s" % d)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows += list(csv.DictReader(fh))
+
+    def short(name):
+        name = re.sub(r"\(.*$", "", name)
+        name = re.sub(r"^void ", "", name)
+        return name.replace("moe::", "").replace("(anonymous namespace)::", "")
+
+    streams = sorted({int(r["Stream_Id"]) for r in rows})
+    groups = {}
+    for r in rows:
+        key = (short(r["Kernel_Name"]), int(r["Stream_Id"]), int(r["Grid_Size_X"]))
+        groups.setdefault(key, []).append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    total = sum(e - s for v in groups.values() for s, e in v)
+    print("| Kernel | Stream | Grid (threads) | Calls | Median (us) | Mean (us) | Min (us) | Max (us) | Share |")
+    print("|---|---|---|---|---|---|---|---|---|")
+    for key, v in sorted(groups.items(), key=lambda kv: -sum(e - s for s, e in kv[1])):
+        durs = sorted((e - s) / 1e3 for s, e in v)
+        print("| `%s` | %d | %d | %d | %.1f | %.1f | %.1f | %.1f | %.2f%% |"
+              % (key[0], key[1], key[2], len(v), durs[len(durs) // 2], sum(durs) / len(durs),
+                 durs[0], durs[-1], 100.0 * sum(durs) * 1e3 / total))
+    if len(streams) > 1:
+        # time the side-stream kernels spend running while a main-stream kernel runs
+        main = sorted((int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                      if int(r["Stream_Id"]) == streams[0])
+        side = [(int(r["Start_Timestamp"]), int(r["End_Timestamp"])) for r in rows
+                if int(r["Stream_Id"]) != streams[0]]
+        busy = ov = 0
+        for s, e in side:
+            busy += e - s
+            for ms, me in main:
+                if me <= s:
+                    continue
+                if ms >= e:
+                    break
+                ov += min(e, me) - max(s, ms)
+        print("\nSide-stream kernels: %.1f us in total, %.1f%% of it beside a main-stream kernel"
+              % (busy / 1e3, 100.0 * ov / max(busy, 1)))
+
+
+# ----------------------------------------------------------------------------- measurement
+
+
 def main():
     a = parse()
+    if a.trace_summary:
+        trace_summary(a.trace_summary)
+        return
     if a.gpus != 1:
         print("bench.py measures one GPU: the library runs the whole MoE layer on a single "
               "MI355X and has no multi-GPU path (--gpus %d requested)" % a.gpus, file=sys.stderr)
@@ -100,172 +193,233 @@ def main():
     from mixture_experts_layer_19_amd import inputs as I
     from mixture_experts_layer_19_amd.layer import DeviceLayer, to_device
 
-    w = I.workload(a.workload)
     dev = torch.device("cuda", 0)
-    t0 = time.time()
-    log("drawing %s weights (E=%d, H=%d, I=%d, %s)" % (w.name, w.E, w.H, w.I, w.dtype))
-    Wg, Wu, Wd = I.all_experts_stored(w)
-    shared = I.shared_stored(w)
-    Wr, bias = I.router_weight(w), I.router_bias(w)
-    log("uploading and packing (%.1fs)" % (time.time() - t0))
-    lay = DeviceLayer(w, expert_fn=lambda e: (Wg[e], Wu[e], Wd[e]), shared_fn=lambda: shared,
-                      router=(Wr, bias), side_stream=not a.single_stream)
     main_stream = torch.cuda.current_stream(dev)
+    flush_buf = None if a.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
-    def run(x_dev, T, steps, warmup):
-        out = torch.empty((T, w.H), dtype=lay.out_dtype(), device=dev)
+    def flush():
+        if flush_buf is not None:
+            flush_buf.fill_(1)      # a fill kernel on the caller's stream, outside the bracket
+
+    def timed(step_fn, steps, warmup):
         for _ in range(warmup):
-            lay.forward(x_dev, out)
+            step_fn()
         torch.cuda.synchronize(dev)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        h0 = time.perf_counter()
-        e0.record(main_stream)
-        for _ in range(steps):
-            lay.forward(x_dev, out)
-        e1.record(main_stream)
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+              for _ in range(steps)]
+        for e0, e1 in ev:
+            flush()
+            e0.record(main_stream)
+            step_fn()
+            e1.record(main_stream)
         torch.cuda.synchronize(dev)
-        wall = (time.perf_counter() - h0) * 1e3
-        return e0.elapsed_time(e1) / steps, wall / steps, out
+        return [e0.elapsed_time(e1) for e0, e1 in ev]
 
-    def run_graph(x_dev, T, steps, warmup):
-        # the same forward captured once as a HIP graph and replayed on the
-        # caller's stream: what a serving loop that records its decode step
-        # would run
-        out = torch.empty((T, w.H), dtype=lay.out_dtype(), device=dev)
-        xs = x_dev.clone()
-        graph = lay.capture(xs, out)
-        for _ in range(warmup):
-            graph.replay()
-        torch.cuda.synchronize(dev)
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
-        e0.record(main_stream)
-        for _ in range(steps):
-            graph.replay()
-        e1.record(main_stream)
-        torch.cuda.synchronize(dev)
-        return e0.elapsed_time(e1) / steps
-
-    def stage_profile(x_dev, T, steps):
+    def stage_profile(lay, x_dev, out, steps):
         B.moe_ctx_set_profiling(lay.ctx, True)
-        out = torch.empty((T, w.H), dtype=lay.out_dtype(), device=dev)
         acc = {}
         for _ in range(steps):
+            flush()
             lay.forward(x_dev, out)
-            ms = B.moe_ctx_stage_ms(lay.ctx)
-            for k, v in ms.items():
-                acc[k] = acc.get(k, 0.0) + v
+            for k, v in B.moe_ctx_stage_ms(lay.ctx).items():
+                acc.setdefault(k, []).append(v)
         B.moe_ctx_set_profiling(lay.ctx, False)
-        return {k: v / steps for k, v in acc.items()}
+        return {k: float(np.median(v)) for k, v in acc.items()}
 
-    def routed_experts(T):
+    def gpu_topk(lay, w, T):
         ws = lay.workspace(T)
         io, _ = B.moe_layer_ws_topk(lay.desc, T)
-        idx = ws[io:io + 4 * T * w.k].view(torch.int32).cpu().numpy()
-        return int(np.unique(idx).size)
+        return ws[io:io + 4 * T * w.k].view(torch.int32).reshape(T, w.k).cpu().numpy()
 
-    # bytes per weight of the routed and the shared experts (MX: + one scale
-    # byte per 32); W4A8 keeps its shared expert in MX-fp8
-    mxw = w.dtype in ("mxfp8", "w4a8")
-    eight = mxw or w.dtype == "fp8"            # 8-bit (or 4-bit) products
-    eb = {"bf16": 2, "f32": 4, "mxfp8": 1, "w4a8": 0.5, "fp8": 1}[w.dtype]
-    ebs = 1 if w.dtype == "w4a8" else eb
-    sb = (1.0 / 32.0) if mxw else 0.0
-    ab = 1 if eight else eb                    # bytes per element of h
-    ob = 4 if w.dtype == "f32" else 2
-    xb = 4 if w.dtype == "f32" else 2
+    orc = None
+    if not (a.no_cpu and a.no_parity):
+        import oracle
+        from oracle import parity as par
+        oracle.build(force=False)
+        orc = oracle
 
-    # ------------------------------------------------------------------ decode-size batch
-    xg, x32 = I.x_input(w)
-    xd = to_device(xg, dev)
-    T = w.T
-    log("timing %s: T=%d, %d warm-up + %d steps" % (w.name, T, a.warmup, a.steps))
-    ms, wall_ms, out_decode = run(xd, T, a.steps, a.warmup)
-    out_host = out_decode.float().cpu().numpy()
-    ws = lay.workspace(T)
-    io, _ = B.moe_layer_ws_topk(lay.desc, T)
-    idx_host = ws[io:io + 4 * T * w.k].view(torch.int32).reshape(T, w.k).cpu().numpy()
-    touched = routed_experts(T)
-    stages = stage_profile(xd, T, a.profile_steps)
-    P = T * w.k
-    # algorithmic bytes: weights of the touched experts, shared expert, router,
-    # activations in, layer output
-    expert_bytes = (3 * w.I * w.H) * (eb + sb)
-    shared_bytes = (3 * w.Is * w.H) * (ebs + sb)
-    layer_bytes = (touched * expert_bytes + shared_bytes + w.E * w.H * 4 + T * w.H * xb
-                   + T * w.H * ob)
-    gu_bytes = touched * (2 * w.I * w.H) * (eb + sb) + T * w.H * xb + P * w.I * (ab + sb)
-    gu_ms = stages["gate_up"]
-    flops = 2.0 * P * 3 * w.I * w.H + 2.0 * T * 3 * w.Is * w.H
-    gu_flops = 2.0 * P * 2 * w.I * w.H
-    tok_s = T / (ms * 1e-3)
-    # MX products run at the fp8 rate (an E2M1 x E4M3 product is priced as fp8)
-    mfma_peak = FP8_PEAK_TFLOPS if eight else BF16_PEAK_TFLOPS
-    if w.name == "hy3_prefill":
-        roof = {"bound": "mfma", "kernel": "routed gate/up + SwiGLU grouped GEMM",
-                "achieved": round(gu_flops / (gu_ms * 1e-3) / 1e12, 1), "peak": mfma_peak,
-                "unit": "TFLOP/s", "frac": round(gu_flops / (gu_ms * 1e-3) / 1e12 / mfma_peak, 4),
-                "traffic": None, "kernel_ms": round(gu_ms, 4), "algorithmic_flops": gu_flops}
-    else:
-        roof = {"bound": "hbm", "kernel": "routed gate/up + SwiGLU grouped GEMM",
-                "achieved": round(gu_bytes / (gu_ms * 1e-3) / 1e9, 1), "peak": HBM_PEAK_GBPS,
-                "unit": "GB/s", "frac": round(gu_bytes / (gu_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                "traffic": measured_traffic(w.name), "kernel_ms": round(gu_ms, 4),
-                "algorithmic_bytes": int(gu_bytes)}
-    result = {
-        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
-        "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "mxfp8-e4m3",
-                  "w4a8": "mxfp4-e2m1 x mxfp8-e4m3", "fp8": "fp8-e4m3 per-tensor"}[w.dtype],
-        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
-        "config": {"workload": w.name, "tokens": T, "hidden": w.H, "experts": w.E,
-                   "top_k": w.k, "inter": w.I, "shared_inter": w.Is,
-                   "touched_experts": touched, "parallelism": "single GPU"},
-        "roofline": roof,
-        "layer": {"algorithmic_bytes": int(layer_bytes),
-                  "hbm_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
-                  "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
-                  "mfma_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
-                  "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / mfma_peak, 4),
-                  "host_wall_ms_per_step": round(wall_ms, 4)},
-        "stages_ms": {k: round(v, 4) for k, v in stages.items()},
-    }
-    if not a.no_graph:
-        gms = run_graph(xd, T, a.steps, a.warmup)
-        result["graph_replay"] = {"ms_per_step": round(gms, 4),
-                                  "tokens_per_s": round(T / (gms * 1e-3), 1),
-                                  "hbm_frac": round(layer_bytes / (gms * 1e-3) / 1e9
-                                                    / HBM_PEAK_GBPS, 4)}
+    def oracle_kw(w):
+        return dict(k=w.k, rho=w.rho, route_norm=w.route_norm,
+                    mx={"mxfp8": 1, "w4a8": 2}.get(w.dtype, 0),
+                    fp8=((w.fp8_x_scale, w.fp8_h_scale, w.fp8_sh_h_scale)
+                         if w.dtype == "fp8" else None))
 
-    # ------------------------------------------------------------------ prefill batch
-    if not a.no_prefill and w.name == "hy3_decode":
-        wp = I.workload("hy3_prefill")
-        lay.w = wp
-        xpg, _ = I.x_input(wp)
-        xpd = to_device(xpg, dev)
-        Tp = wp.T
-        log("timing hy3_prefill: T=%d" % Tp)
-        msp, _, _ = run(xpd, Tp, max(5, a.steps // 5), max(2, a.warmup // 2))
-        stp = stage_profile(xpd, Tp, max(3, a.profile_steps // 4))
-        Pp = Tp * wp.k
-        fl = 2.0 * Pp * 3 * wp.I * wp.H + 2.0 * Tp * 3 * wp.Is * wp.H
-        gu_fl = 2.0 * Pp * 2 * wp.I * wp.H
-        result["prefill"] = {
-            "workload": wp.name, "tokens": Tp, "ms_per_step": round(msp, 4),
-            "tokens_per_s": round(Tp / (msp * 1e-3), 1),
-            "mfma_TFLOPs": round(fl / (msp * 1e-3) / 1e12, 1),
-            "mfma_frac": round(fl / (msp * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-            "roofline": {"bound": "mfma", "kernel": "routed gate/up + SwiGLU grouped GEMM",
-                         "achieved": round(gu_fl / (stp["gate_up"] * 1e-3) / 1e12, 1),
-                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(gu_fl / (stp["gate_up"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel_ms": round(stp["gate_up"], 4)},
-            "stages_ms": {k: round(v, 4) for k, v in stp.items()},
-        }
+    def expert_cache(w):
+        cache = {}
+
+        def get(e):
+            if e not in cache:
+                cache[e] = I.expert_stored(w, e)
+            return cache[e]
+        return get
+
+    def parity_sample(w, x32, out_host, g_idx, toks):
+        """The oracle on tokens `toks` of the timed batch, with the tie rule
+        and flipped tokens evaluated with the GPU's selection."""
+        Wr, b = I.router_weight(w), I.router_bias(w)
+        xs = x32[toks]
+        o_idx, _, scores, _ = orc.route(xs, Wr, b, w.k, w.rho, w.route_norm)
+        mism, flips = par.classify_routing(g_idx[toks], o_idx, scores)
+        get = expert_cache(w)
+        sh = I.shared_stored(w) if w.Is else None
+        sel = np.where(flips[:, None], g_idx[toks], o_idx)
+        ok = ~mism | flips
+        ref, _, _, _ = orc.layer_forward_tokens(toks[ok], x32, Wr, b, get, sh, topk_idx=sel[ok],
+                                                **oracle_kw(w))
+        got = out_host[toks[ok]].astype(np.float64)
+        err = float(np.abs(got - ref).max() / np.abs(ref).max()) if ok.any() else None
+        return {"tokens": int(len(toks)), "index_mismatches": int(mism.sum()),
+                "tie_flips": int(flips.sum()), "non_tie_mismatches": int((mism & ~flips).sum()),
+                "max_rel_err": None if err is None else float("%.3g" % err),
+                "tolerance": {"f32": 1e-5, "bf16": 1e-2}.get(w.dtype, 3e-2)}
+
+    def bytes_per_weight(w):
+        # routed and shared expert weights (MX: + one scale byte per 32; the
+        # shared expert of a W4A8 layer is MX-fp8)
+        mxw = w.dtype in ("mxfp8", "w4a8")
+        eb = {"bf16": 2, "f32": 4, "mxfp8": 1, "w4a8": 0.5, "fp8": 1}[w.dtype]
+        ebs = 1 if w.dtype == "w4a8" else eb
+        sb = (1.0 / 32.0) if mxw else 0.0
+        return eb + sb, ebs + sb
+
+    def run_workload(w, lay, headline=False):
+        T = w.T
         lay.w = w
-        del xpd
+        xg, x32 = I.x_input(w)
+        x_dev = to_device(xg, dev)
+        out = torch.empty((T, w.H), dtype=lay.out_dtype(), device=dev)
+        log("timing %s: T=%d, %d warm-up + %d steps" % (w.name, T, a.warmup, a.steps))
+        wall0 = time.perf_counter()
+        ts = timed(lambda: lay.forward(x_dev, out), a.steps, a.warmup)
+        wall = (time.perf_counter() - wall0) * 1e3 / (a.steps + a.warmup)
+        torch.cuda.synchronize(dev)
+        out_host = out.float().cpu().numpy()
+        g_idx = gpu_topk(lay, w, T)
+        touched = int(np.unique(g_idx).size)
+        stages = stage_profile(lay, x_dev, out, a.profile_steps)
+        ms = float(np.median(ts))
+        P = T * w.k
+        ew, ews = bytes_per_weight(w)
+        eight = w.dtype in ("mxfp8", "w4a8", "fp8")
+        ab = 1 if eight else {"f32": 4}.get(w.dtype, 2)       # bytes per element of x, h
+        xb = 4 if w.dtype == "f32" else 2
+        ob = xb
+        layer_bytes = (touched * 3 * w.I * w.H * ew + 3 * w.Is * w.H * ews + w.E * w.H * 4
+                       + T * w.H * xb + T * w.H * ob)
+        flops = 2.0 * P * 3 * w.I * w.H + 2.0 * T * 3 * w.Is * w.H
+        gu_bytes = touched * 2 * w.I * w.H * ew + T * w.H * xb + P * w.I * ab
+        gu_flops = 2.0 * P * 2 * w.I * w.H
+        gu_ms = stages["gate_up"]
+        mfma_peak = (FP8_PEAK_TFLOPS if eight else FP32_PEAK_TFLOPS if w.dtype == "f32"
+                     else BF16_PEAK_TFLOPS)
+        if w.name in MFMA_BOUND:
+            ach = gu_flops / (gu_ms * 1e-3) / 1e12
+            roof = {"bound": "mfma", "kernel": "routed gate/up + SwiGLU grouped GEMM",
+                    "achieved": round(ach, 1), "peak": mfma_peak, "unit": "TFLOP/s",
+                    "frac": round(ach / mfma_peak, 4), "traffic": None,
+                    "kernel_ms": round(gu_ms, 4), "algorithmic_flops": gu_flops}
+        else:
+            ach = gu_bytes / (gu_ms * 1e-3) / 1e9
+            roof = {"bound": "hbm", "kernel": "routed gate/up + SwiGLU grouped GEMM",
+                    "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                    "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
+                    "kernel_ms": round(gu_ms, 4), "algorithmic_bytes": int(gu_bytes)}
+        res = {
+            "workload": w.name, "tokens": T, "hidden": w.H, "experts": w.E, "top_k": w.k,
+            "inter": w.I, "shared_inter": w.Is, "dtype": w.dtype, "touched_experts": touched,
+            "ms_per_step": round(ms, 4), "p10_ms": round(pct(ts, 10), 4),
+            "p90_ms": round(pct(ts, 90), 4), "tokens_per_s": round(T / (ms * 1e-3), 1),
+            "roofline": roof,
+            "layer": {"algorithmic_bytes": int(layer_bytes),
+                      "hbm_GBps": round(layer_bytes / (ms * 1e-3) / 1e9, 1),
+                      "hbm_frac": round(layer_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBPS, 4),
+                      "algorithmic_flops": flops,
+                      "mfma_TFLOPs": round(flops / (ms * 1e-3) / 1e12, 2),
+                      "mfma_peak": mfma_peak,
+                      "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / mfma_peak, 4),
+                      "host_wall_ms_per_step": round(wall, 4)},
+            "stages_ms": {k: round(v, 4) for k, v in stages.items()},
+        }
+        if w.name == "hy4_skew":
+            counts = np.bincount(g_idx.ravel(), minlength=w.E)
+            res["load"] = {"max_rows": int(counts.max()), "mean_rows": float(counts.mean()),
+                           "max_over_mean": round(float(counts.max() / counts.mean()), 2)}
+        if not a.no_graph:
+            xs = x_dev.clone()
+            graph = lay.capture(xs, out)
+            gt = timed(graph.replay, a.steps, a.warmup)
+            gms = float(np.median(gt))
+            res["graph_replay"] = {"ms_per_step": round(gms, 4), "p10_ms": round(pct(gt, 10), 4),
+                                   "p90_ms": round(pct(gt, 90), 4),
+                                   "tokens_per_s": round(T / (gms * 1e-3), 1)}
+            del graph
+        if orc is not None and not a.no_parity:
+            if T <= 64:
+                toks = np.arange(T)
+            else:
+                rng = np.random.default_rng(12345)
+                toks = np.unique(np.concatenate([np.arange(8), np.arange(T - 8, T),
+                                                 rng.choice(T, 16, replace=False)]))
+            t0 = time.perf_counter()
+            res["parity"] = parity_sample(w, x32, out_host, g_idx, toks)
+            log("%s parity on %d tokens: %s (%.1fs)" % (w.name, len(toks), res["parity"],
+                                                      time.perf_counter() - t0))
+        if headline and orc is not None and not a.no_cpu:
+            res["cpu_baseline"] = cpu_baseline(w, x32)
+        del x_dev, out
+        return res
+
+    def cpu_baseline(w, x32):
+        # the oracle as it stands on a bounded sample: the first n tokens of
+        # the batch (all of them when the batch is small), `reps` passes
+        Wr, b = I.router_weight(w), I.router_bias(w)
+        get = expert_cache(w)
+        sh = I.shared_stored(w) if w.Is else None
+        kw = oracle_kw(w)
+
+        def run(n):
+            return orc.layer_forward_tokens(np.arange(n), x32, Wr, b, get, sh, **kw)
+
+        t1 = time.perf_counter()
+        run(1)
+        one = time.perf_counter() - t1
+        n = int(max(1, min(w.T, a.cpu_seconds / max(one, 1e-3))))
+        run(n)                                          # draws the experts the sample needs
+        t1 = time.perf_counter()
+        run(n)
+        first = time.perf_counter() - t1
+        reps = int(max(1, min(100, a.cpu_seconds / max(first, 1e-3))))
+        t1 = time.perf_counter()
+        for _ in range(reps):
+            run(n)
+        dt = time.perf_counter() - t1
+        flops_tok = 2.0 * w.E * w.H + 2.0 * w.k * 3 * w.I * w.H + 2.0 * 3 * w.Is * w.H
+        return {"value": round(n * reps / dt, 3), "unit": "tokens/s",
+                "cores": orc.num_threads(), "kind": "oracle", "cpu_model": cpu_model(),
+                "gflops": round(flops_tok * n * reps / dt / 1e9, 2),
+                "sample": "first %d of the %d tokens of the %s batch, %d passes: fp64-accumulating "
+                          "C oracle (gating, each token's %d expert FFNs, shared FFN, combine); "
+                          "%.1f s" % (n, w.T, w.name, reps, w.k, dt)}
+
+    names = DEFAULT_WORKLOADS if a.workload == "all" else [a.workload]
+    headline = names[0]
+    results = {}
+    layers = {}
+    for name in names:
+        w = I.workload(name)
+        key = (w.H, w.E, w.k, w.I, w.Is, w.dtype, w.seed, w.zipf_beta)
+        if key not in layers:
+            for k in list(layers):                    # one weight set on the device at a time
+                layers.pop(k).close()
+            torch.cuda.empty_cache()
+            t0 = time.time()
+            log("drawing and packing %s weights (E=%d, H=%d, I=%d, %s)" % (w.name, w.E, w.H, w.I,
+                                                                           w.dtype))
+            layers[key] = DeviceLayer(w, side_stream=not a.single_stream)
+            log("packed in %.1fs" % (time.time() - t0))
+        results[name] = run_workload(w, layers[key], headline=(name == headline))
+    for lay in layers.values():
+        lay.close()
 
     if a.copy_calib:
         # plain device copy of a known size, for HBM counter calibration
@@ -277,55 +431,30 @@ def main():
         torch.cuda.synchronize(dev)
         del src, dst
 
-    # ------------------------------------------------------------------ CPU oracle
-    if not a.no_cpu:
-        import oracle
-        oracle.build(force=False)
-
-        def oracle_tokens(toks):
-            return oracle.layer_forward_tokens(toks, x32, Wr, bias, lambda e: (Wg[e], Wu[e], Wd[e]),
-                                        shared, k=w.k, rho=w.rho, route_norm=w.route_norm,
-                                        mx={"mxfp8": 1, "w4a8": 2}.get(w.dtype, 0),
-                                        fp8=((w.fp8_x_scale, w.fp8_h_scale, w.fp8_sh_h_scale)
-                                             if w.dtype == "fp8" else None))
-
-        # a bounded sample: the first n tokens of the batch (all of them when
-        # the batch is small), evaluated `reps` times back to back
-        t1 = time.perf_counter()
-        oracle_tokens(np.arange(1))
-        one = time.perf_counter() - t1
-        n = int(max(1, min(T, a.cpu_seconds / max(one, 1e-3))))
-        t1 = time.perf_counter()
-        oracle_tokens(np.arange(n))
-        first = time.perf_counter() - t1
-        reps = int(max(1, min(100, a.cpu_seconds / max(first, 1e-3))))
-        t1 = time.perf_counter()
-        for _ in range(reps):
-            oracle_tokens(np.arange(n))
-        dt = time.perf_counter() - t1
-        # parity of the timed batch on the same sample: routing indices
-        # (mismatches, and those inside the oracle's 1e-6 score gap at the
-        # top-k boundary, i.e. tie flips) and the output relative to the
-        # largest oracle magnitude, over the tokens whose routing agrees
-        ref, o_idx, _, gap = oracle_tokens(np.arange(n))
-        mism = (idx_host[:n] != o_idx).any(axis=1)
-        keep = ~mism
-        err = (float(np.abs(out_host[:n][keep].astype(np.float64) - ref[keep]).max()
-                     / np.abs(ref[keep]).max()) if keep.any() else None)
-        result["parity"] = {
-            "tokens": n, "index_mismatches": int(mism.sum()),
-            "tie_flips": int((mism & (gap <= 1e-6)).sum()),
-            "max_rel_err": None if err is None else float("%.3g" % err),
-            "tolerance": {"f32": 1e-5, "bf16": 1e-2}.get(w.dtype, 3e-2)}
-        result["cpu_baseline"] = {
-            "value": round(n * reps / dt, 3), "unit": "tokens/s", "cores": oracle.num_threads(),
-            "kind": "oracle",
-            "sample": "first %d of the %d tokens of the %s batch, %d passes: fp64-accumulating "
-                      "C oracle (gating, each token's %d expert FFNs, shared FFN, combine); "
-                      "%.1f s" % (n, T, w.name, reps, w.k, dt)}
-
-    lay.close()
-    print(json.dumps(result), flush=True)
+    h = results[headline]
+    hw = I.workload(headline)
+    line = {
+        "metric": METRIC, "value": h["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+        "steps": a.steps, "warmup": a.warmup, "ms_per_step": h["ms_per_step"],
+        "p10_ms": h["p10_ms"], "p90_ms": h["p90_ms"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": {"bf16": "bf16", "f32": "f32", "mxfp8": "mxfp8-e4m3",
+                  "w4a8": "mxfp4-e2m1 x mxfp8-e4m3", "fp8": "fp8-e4m3 per-tensor"}[hw.dtype],
+        "data": "synthetic (seeded N(0,1) activations, N(0,0.02) weights)",
+        "config": {"workload": hw.name, "tokens": hw.T, "hidden": hw.H, "experts": hw.E,
+                   "top_k": hw.k, "inter": hw.I, "shared_inter": hw.Is,
+                   "touched_experts": h["touched_experts"], "parallelism": "single GPU",
+                   "timing": "median of %d steps, caches evicted before each" % a.steps
+                             if not a.no_flush else "median of %d steps" % a.steps},
+        "roofline": h["roofline"],
+        "layer": h["layer"],
+        "stages_ms": h["stages_ms"],
+    }
+    for k in ("graph_replay", "parity", "cpu_baseline"):
+        if k in h:
+            line[k] = h[k]
+    line["workloads"] = {n: r for n, r in results.items() if n != headline}
+    print(json.dumps(line), flush=True)
 
 
 if __name__ == "__main__":
