@@ -265,6 +265,24 @@ MOE_API moe_status moe_ctx_stage_ms(moe_ctx *ctx, float *ms /* host, MOE_NUM_STA
 MOE_API moe_status moe_layer_ws_topk(const moe_desc *desc /* host */, int32_t T,
                              size_t *idx_offset /* host */, size_t *w_offset /* host */);
 
+/* moe_layer_forward with no caller workspace and no allocation, for callers
+ * that cannot call hipMalloc: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation.  The workspace is a static device
+ * array of MOE_NOALLOC_SCRATCH_BYTES (64 MiB) inside the library, one copy
+ * per GPU, held until the process ends; moe_ctx_create looks up its address
+ * on the context's device.  Arguments and results are those of
+ * moe_layer_forward.  If moe_workspace_bytes(desc, T, MOE_WS_LAYER) exceeds
+ * the array the call returns MOE_ERR_WORKSPACE (text in moe_ctx_last_error)
+ * and enqueues nothing; for the Hy3 shape in bf16 (H = 4096, E = 192, k = 8,
+ * I = I_s = 1536) that admits up to T = 548 tokens (64 tokens use 11.5 MiB).  Every call on one GPU
+ * shares the array and leaves its contents behind: calls that can overlap on
+ * one GPU (other streams or contexts without ordering between them) race and
+ * give undefined results.  Nothing in the array needs to start at zero. */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+MOE_API moe_status moe_layer_forward_noalloc(moe_ctx *ctx, const moe_desc *desc /* host */,
+                                     const moe_weights *w /* host */, const void *x, int32_t T,
+                                     void *out, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

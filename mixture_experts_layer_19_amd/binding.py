@@ -25,7 +25,8 @@ EXPORTS = ("moe_ctx_create", "moe_ctx_destroy", "moe_status_string", "moe_ctx_la
            "moe_workspace_bytes", "moe_packed_bytes", "moe_pack_experts", "moe_mx_quantize",
            "moe_fp8_quantize",
            "moe_route", "moe_permute", "moe_grouped_ffn", "moe_combine", "moe_layer_forward",
-           "moe_layer_ws_topk", "moe_ctx_set_profiling", "moe_ctx_stage_ms")
+           "moe_layer_ws_topk", "moe_ctx_set_profiling", "moe_ctx_stage_ms",
+           "moe_layer_forward_noalloc")
 STAGES = ("route", "mx_quant", "permute", "gate_up", "down", "shared_gate_up", "shared_down",
           "combine")
 
@@ -82,6 +83,7 @@ def lib():
             "moe_grouped_ffn": ([P, DP, WP, ctypes.c_int, P, I32, P, P, P, P, S, P], ctypes.c_int),
             "moe_combine": ([P, DP, P, P, P, P, I32, P, P], ctypes.c_int),
             "moe_layer_forward": ([P, DP, WP, P, I32, P, P, S, P], ctypes.c_int),
+            "moe_layer_forward_noalloc": ([P, DP, WP, P, I32, P, P], ctypes.c_int),
             "moe_layer_ws_topk": ([DP, I32, ctypes.POINTER(S), ctypes.POINTER(S)], ctypes.c_int),
             "moe_ctx_set_profiling": ([P, ctypes.c_int], ctypes.c_int),
             "moe_ctx_stage_ms": ([P, ctypes.POINTER(ctypes.c_float)], ctypes.c_int),
@@ -190,6 +192,15 @@ def moe_combine(ctx, desc, y, dest, topk_w, shared_out, T, out, stream=None):
 def moe_layer_forward(ctx, desc, weights, x, T, out, ws, ws_bytes, stream=None):
     _check(lib().moe_layer_forward(ctx, ctypes.byref(desc), ctypes.byref(weights), _ptr(x), T,
                                    _ptr(out), _ptr(ws), ws_bytes, _stream(stream)), ctx)
+
+
+def moe_layer_forward_noalloc(ctx, desc, weights, x, T, out, stream=None):
+    _check(lib().moe_layer_forward_noalloc(ctx, ctypes.byref(desc), ctypes.byref(weights),
+                                           _ptr(x), T, _ptr(out), _stream(stream)), ctx)
+
+
+# bytes of the static workspace moe_layer_forward_noalloc uses (include/moe.h)
+MOE_NOALLOC_SCRATCH_BYTES = 64 << 20
 
 
 def moe_layer_ws_topk(desc, T):

@@ -14,6 +14,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
@@ -23,6 +25,19 @@
 #ifndef MOE_SHARED_EARLY_T
 #define MOE_SHARED_EARLY_T 64
 #endif
+
+// Workspace of moe_layer_forward_noalloc: a static device array (one copy
+// per GPU, held until the process ends).  In host code `scratch` names a
+// host-side stand-in, not the device memory: its device address on each GPU
+// comes from hipGetSymbolAddress (moe_ctx_create, with the device current)
+// and only that address is ever passed to kernels.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch[kMaxDevices];     // device address of `scratch` per device, or null
+}  // namespace
 
 struct moe_ctx {
   int device;
@@ -302,6 +317,22 @@ moe_status moe_ctx_create(int device, void *side_stream, moe_ctx **out) {
   int cur = -1;
   if (hipGetDevice(&cur) != hipSuccess) return MOE_ERR_DEVICE;
   if (cur != device && hipSetDevice(device) != hipSuccess) return MOE_ERR_DEVICE;
+  if (device >= kMaxDevices) {
+    if (cur != device) (void)hipSetDevice(cur);
+    return MOE_ERR_DEVICE;
+  }
+  {
+    // the no-allocation entry point's workspace on this device (current now)
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch[device]) {
+      void *p = nullptr;
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+        if (cur != device) (void)hipSetDevice(cur);
+        return MOE_ERR_DEVICE;
+      }
+      g_scratch[device] = p;
+    }
+  }
   moe_ctx *c = new (std::nothrow) moe_ctx;
   if (!c) return MOE_ERR_DEVICE;
   memset(c, 0, sizeof *c);
@@ -647,6 +678,30 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   MOE_TRY(tm.stop(MOE_STAGE_COMBINE, s), "timing");
 #undef MOE_TRY
   return MOE_OK;
+}
+
+moe_status moe_layer_forward_noalloc(moe_ctx *ctx, const moe_desc *desc, const moe_weights *w,
+                                     const void *x, int32_t T, void *out, void *stream) {
+  moe_status st = check_desc(desc);
+  if (st != MOE_OK) return st;
+  if ((st = check_ctx(ctx)) != MOE_OK) return st;
+  if (T < 0) return MOE_ERR_INVALID_ARG;
+  if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
+  const size_t need = layout(desc, T, MOE_WS_LAYER).total;
+  if (need > MOE_NOALLOC_SCRATCH_BYTES) {
+    snprintf(ctx->last_error, sizeof ctx->last_error,
+             "moe_layer_forward_noalloc: %d tokens need %zu bytes of workspace, above the "
+             "%zu-byte static scratch",
+             (int)T, need, (size_t)MOE_NOALLOC_SCRATCH_BYTES);
+    return MOE_ERR_WORKSPACE;
+  }
+  void *ws;
+  {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ws = g_scratch[ctx->device];
+  }
+  if (!ws) return MOE_ERR_DEVICE;
+  return moe_layer_forward(ctx, desc, w, x, T, out, ws, MOE_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

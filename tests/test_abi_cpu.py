@@ -119,6 +119,15 @@ def test_null_context_is_rejected(B):
     with pytest.raises(B.MoeError) as ei:
         B.moe_route(None, d, 1, 4, 1, None, 1, 1, 1, 1 << 30)
     assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_layer_forward_noalloc(None, d, B.MoeWeights(), 1, 4, 1)
+    assert ei.value.status == B.MOE_ERR_INVALID_ARG
+
+
+def test_noalloc_scratch_size_matches_header(B):
+    hdr = open(os.path.join(ROOT, "include", "moe.h")).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in hdr
+    assert B.MOE_NOALLOC_SCRATCH_BYTES == 64 << 20
 
 
 def test_w4a8_and_fp8_packed_sizes(B):
