@@ -70,6 +70,8 @@ def parse():
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="summarise the rocprofv3 kernel trace under DIR and exit")
+    ap.add_argument("--counter-summary", metavar="DIR", nargs="+",
+                    help="summarise rocprofv3 --pmc outputs under DIR(s) and exit")
     return ap.parse_args()
 
 
@@ -96,7 +98,6 @@ def measured_traffic(workload: str):
     """HBM bytes per launch of the decode gate/up kernel from the committed
     rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel's
     source has changed since those counters were taken."""
-    import hashlib
     if workload != "hy3_decode":
         return None
     path = os.path.join(ROOT, "profiles", "hy3_decode_gate_up_traffic.txt")
@@ -108,12 +109,7 @@ def measured_traffic(workload: str):
             continue
         k, v = line.split(":", 1)
         kv[k.strip()] = v.strip()
-    h = hashlib.sha256()
-    for f in ("mixture_experts_layer_19_amd/csrc/gemm.hip",
-              "mixture_experts_layer_19_amd/csrc/gemm_common.hpp",
-              "mixture_experts_layer_19_amd/csrc/moe_common.hpp"):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
-    if kv.get("source_sha256") != h.hexdigest():
+    if kv.get("source_sha256") != gemm_source_sha256():
         return None
     return int(kv["traffic_bytes"])
 
@@ -173,6 +169,69 @@ def trace_summary(d: str) -> None:
               % (busy / 1e3, 100.0 * ov / max(busy, 1)))
 
 
+def gemm_source_sha256() -> str:
+    """SHA-256 of the grouped GEMM sources (to tie counter readings to a build)."""
+    import hashlib
+    h = hashlib.sha256()
+    for f in ("mixture_experts_layer_19_amd/csrc/gemm.hip",
+              "mixture_experts_layer_19_amd/csrc/gemm_common.hpp",
+              "mixture_experts_layer_19_amd/csrc/moe_common.hpp"):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    return h.hexdigest()
+
+
+def counter_summary(dirs) -> None:
+    """Mean per dispatch of every counter in rocprofv3 --pmc outputs, by kernel
+    and grid size.  FETCH_SIZE / WRITE_SIZE (KiB) are also converted to bytes
+    with the factor that makes a 1 GiB device copy in the same run (the
+    largest __amd_rocclr_copyBuffer dispatch) read or write 1 GiB."""
+    import csv
+    import glob
+    import re
+    rows = []
+    for d in dirs:
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(f) as fh:
+                rows += list(csv.DictReader(fh))
+    if not rows:
+        sys.exit("no *counter_collection.csv under %s" % " ".join(dirs))
+
+    def short(name):
+        name = re.sub(r"\(.*$", "", name)
+        return re.sub(r"^void ", "", name).replace("moe::", "")
+
+    vals = {}
+    for r in rows:
+        key = (short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        vals.setdefault(key, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    factor = {}
+    for c in ("FETCH_SIZE", "WRITE_SIZE"):
+        copies = [max(v[c]) for (n, _), v in vals.items() if n == "__amd_rocclr_copyBuffer" and c in v]
+        if copies and max(copies) > 0:
+            factor[c] = (1 << 30) / (max(copies) * 1024.0)
+    counters = sorted({c for v in vals.values() for c in v})
+    print("GEMM source sha256: %s" % gemm_source_sha256())
+    for c, f in factor.items():
+        print("%s calibration: bytes = KiB x 1024 x %.4f (1 GiB copy)" % (c, f))
+    print()
+    print("| Kernel | Grid | Dispatches | " + " | ".join(counters) + " |")
+    print("|---|---|---|" + "---|" * len(counters))
+    for key in sorted(vals, key=lambda k: (k[0], k[1])):
+        v = vals[key]
+        n = max(len(x) for x in v.values())
+        cells = []
+        for c in counters:
+            if c not in v:
+                cells.append("")
+                continue
+            m = sum(v[c]) / len(v[c])
+            cell = "%.1f" % m
+            if c in factor:
+                cell += " (%.3f GB)" % (m * 1024.0 * factor[c] / 1e9)
+            cells.append(cell)
+        print("| `%s` | %d | %d | %s |" % (key[0], key[1], n, " | ".join(cells)))
+
+
 # ----------------------------------------------------------------------------- measurement
 
 
@@ -180,6 +239,9 @@ def main():
     a = parse()
     if a.trace_summary:
         trace_summary(a.trace_summary)
+        return
+    if a.counter_summary:
+        counter_summary(a.counter_summary)
         return
     if a.gpus != 1:
         print("bench.py measures one GPU: the library runs the whole MoE layer on a single "

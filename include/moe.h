@@ -230,12 +230,17 @@ MOE_API moe_status moe_combine(moe_ctx *ctx, const moe_desc *desc /* host */, co
                        void *out, void *stream);
 
 /* The whole layer on `stream` (Hy3 guide, section 8.5 two-stream schedule):
- * (MX-fp8 only: quantise x;) gating, permutation and the routed gate/up
- * GEMM on `stream`, then the input-ready event; the side stream waits on it
- * and runs the shared expert beside the routed down GEMM, then records the
- * shared-done event, which `stream` waits on before the combine.  On return
- * `stream` has been made to wait for the side stream, so work queued on
- * `stream` afterwards sees the finished layer.
+ * (8-bit and MXFP4 experts: quantise x;) gating, permutation and the routed
+ * gate/up GEMM on `stream`, then the input-ready event; the side stream
+ * waits on it and runs the shared expert beside the routed down GEMM, then
+ * records the shared-done event, which `stream` waits on before the
+ * combine.  The side stream is used where the overlap was measured to pay:
+ * not for a shared expert under 1 MiB of weights (launch-bound layers), and
+ * not at 256 or more rows per routed expert (T * k >= 256 * E, where every
+ * GEMM is bound by the matrix cores); there the shared expert runs on
+ * `stream` in the same place.  On return `stream` has been made to wait for
+ * the side stream, so work queued on `stream` afterwards sees the finished
+ * layer.
  *   x [T,H] (act_dtype), out [T,H] (out_dtype).
  * ws: moe_workspace_bytes(desc, T, MOE_WS_LAYER) bytes; its layout is
  * internal, except that moe_layer_ws_topk() locates the routing result. */

@@ -12,8 +12,7 @@ import os
 import threading
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-# MOE_LIBMOE may name another build of the same library (a tuning variant)
-LIB_PATH = os.environ.get("MOE_LIBMOE") or os.path.join(HERE, "libmoe.so")
+LIB_PATH = os.path.join(HERE, "libmoe.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE, MOE_ERR_DEVICE = range(5)
 MOE_F32, MOE_BF16, MOE_MXFP8, MOE_MXFP4, MOE_FP8 = 0, 1, 2, 3, 4

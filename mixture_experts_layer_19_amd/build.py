@@ -26,17 +26,16 @@ def _hipcc() -> str:
     return p
 
 
-def build(verbose: bool = False, defines=(), out: str = LIB) -> str:
+def build(verbose: bool = False, out: str = LIB) -> str:
     """Compile csrc/*.hip and link them into `out` (default: the package's
-    libmoe.so).  `defines` are extra -D macros (tuning variants)."""
+    libmoe.so)."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
-    tag = "_".join(d.replace("=", "") for d in defines)
-    objdir = os.path.join(HERE, "_build" + ("_" + tag if tag else ""))
+    objdir = os.path.join(HERE, "_build")
     os.makedirs(objdir, exist_ok=True)
     flags = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-fvisibility=hidden",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I", os.path.join(ROOT, "include"), "-Wall", "-Wno-unused-function",
-             "-Wno-unused-variable"] + ["-D" + d for d in defines]
+             "-Wno-unused-variable"]
     hipcc = _hipcc()
 
     def one(src):
@@ -64,8 +63,7 @@ if __name__ == "__main__":
     import argparse
     import time
     ap = argparse.ArgumentParser()
-    ap.add_argument("-D", dest="defines", action="append", default=[])
     ap.add_argument("-o", dest="out", default=LIB)
     a = ap.parse_args()
     t = time.time()
-    print(build(verbose=True, defines=a.defines, out=a.out), "%.1fs" % (time.time() - t))
+    print(build(verbose=True, out=a.out), "%.1fs" % (time.time() - t))

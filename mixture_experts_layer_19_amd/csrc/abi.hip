@@ -20,11 +20,10 @@
 #include "moe_common.hpp"
 #include "moe_launch.hpp"
 
-// Batches of at most this many tokens start the shared expert on the side
-// stream before gating; larger ones start it beside the routed down GEMM.
-#ifndef MOE_SHARED_EARLY_T
-#define MOE_SHARED_EARLY_T 64
-#endif
+// Batches of at most this many tokens with 8- or 4-bit experts start the
+// shared expert on the side stream before gating; the others start it beside
+// the routed down GEMM.
+constexpr int kSharedEarlyT = 64;
 
 // Workspace of moe_layer_forward_noalloc: a static device array (one copy
 // per GPU, held until the process ends).  In host code `scratch` names a
@@ -86,6 +85,11 @@ size_t act_bytes(const moe_desc *d) {
   return (mx_act(d) || fp8_act(d)) ? 1 : elem_bytes(d->expert_dtype);
 }
 bool good_scale(float v) { return v > 0.0f && v < 3.0e38f; }
+// moe_dtype of the routed (shared = 0) or shared experts' weights (the shared
+// expert of a W4A8 layer is MX-fp8).
+int weight_fmt_dtype(const moe_desc *d, int shared) {
+  return (d->expert_dtype == MOE_MXFP4 && shared) ? MOE_MXFP8 : d->expert_dtype;
+}
 
 // Shape and dtype checks shared by every entry point.
 moe_status check_desc(const moe_desc *d) {
@@ -631,13 +635,34 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   // input-ready event is recorded after it), so it runs beside the routed
   // down GEMM: beside gating and permutation it slows those short,
   // latency-bound kernels by more than it saves.  For decode-sized batches
-  // (T <= MOE_SHARED_EARLY_T) with 8- or 4-bit experts it starts at once,
+  // (T <= kSharedEarlyT) with 8- or 4-bit experts it starts at once,
   // beside gating and the routed gate/up GEMM: there the routed down GEMM
   // is shorter than the 8-bit shared expert, which would otherwise lengthen
   // the layer (W4A8 decode 0.398 -> 0.370 ms).  A bf16 decode batch keeps
   // the late start (the early one slows gating, +0.4%).
-  const bool two = has_shared && ctx->side && ctx->side != s;
-  const bool early = two && (mx || fp8_act(desc)) && T <= MOE_SHARED_EARLY_T;
+  //
+  // The side stream is used where the overlap pays.  The HunyuanImage-3.0
+  // article (caveats) warns that under contention the second stream may not
+  // lower the wall time, and that is what was measured at the two ends
+  // (layer time, two streams against one, same build):
+  //  * a layer whose shared expert holds under 1 MiB of weights is bound by
+  //    launch latency, and the cross-stream events cost more than the
+  //    overlap saves (fp32 H = 256 layer: 0.093 ms against 0.076);
+  //  * with 256 or more rows per routed expert every GEMM is bound by the
+  //    matrix cores and the shared expert's tiles only compete with the
+  //    routed down GEMM's (Hy3 prefill, 341 rows per expert: 3.204 ms
+  //    against 3.163);
+  //  * in between the overlap pays: Hy3 decode 1.088 against 1.097 ms,
+  //    Hy4-skew (64 rows per expert) 2.084 against 2.120, MX-fp8 at 4096
+  //    tokens (171 rows per expert) 1.393 against 1.433.
+  // Otherwise the shared expert runs on the caller's stream, in the same
+  // place in the order.
+  const size_t shared_weight_bytes =
+      (size_t)3 * H * desc->shared_inter * elem_bytes(weight_fmt_dtype(desc, 1));
+  const bool side_pays = shared_weight_bytes >= ((size_t)1 << 20) &&
+                         (long long)T * k < 256LL * E;
+  const bool two = has_shared && ctx->side && ctx->side != s && side_pays;
+  const bool early = two && (mx || fp8_act(desc)) && T <= kSharedEarlyT;
   auto shared_expert = [&]() -> hipError_t {
     hipStream_t ss = two ? ctx->side : s;
     hipError_t e;

@@ -25,9 +25,8 @@
 // per-tensor scales, which the epilogue applies.
 #include "gemm_common.hpp"
 
-#ifndef MOE_TILE_MAP
-#define MOE_TILE_MAP 0
-#endif
+namespace moe {
+
 // Decode streaming kernel: weight blocks per wave, and the dynamic LDS
 // reserved per workgroup (the kernel uses none), which caps its residency.
 // Fewer concurrent weight streams read HBM faster than a full CU, and leave
@@ -41,68 +40,22 @@
 //  * E2M1 weights: 8 blocks per wave for the gate/up GEMM, whose blocks are
 //    half as large (0.212 -> 0.205 ms against 4), 2 for the down GEMM, at 5
 //    workgroups per CU (layer 0.367 -> 0.363 ms against 4 blocks at 3).
-#ifndef MOE_SKINNY_LDS_PAD
-#define MOE_SKINNY_LDS_PAD 30000
-#endif
-#ifndef MOE_SKINNY_LDS_PAD_8BIT
-#define MOE_SKINNY_LDS_PAD_8BIT 45000
-#endif
-#ifndef MOE_SKINNY_NW
-#define MOE_SKINNY_NW 2
-#endif
-#ifndef MOE_SKINNY_NW_8BIT
-#define MOE_SKINNY_NW_8BIT 4
-#endif
-#ifndef MOE_SKINNY_NW_MX4
-#define MOE_SKINNY_NW_MX4 8
-#endif
-#ifndef MOE_SKINNY_PF
-#define MOE_SKINNY_PF 0
-#endif
+constexpr int kSkinnyLdsPad = 30000, kSkinnyLdsPad8 = 45000;
+constexpr int kSkinnyNW = 2, kSkinnyNW8 = 4, kSkinnyNWMx4 = 8;
 // streaming kernel for the short segments of a mixed launch: weight blocks
-// per wave, token blocks per pass
-#ifndef MOE_HYB_NW
-#define MOE_HYB_NW 4
-#endif
-#ifndef MOE_HYB_MB
-#define MOE_HYB_MB 2
-#endif
-#ifndef MOE_HYB_SPLIT
-#define MOE_HYB_SPLIT 32
-#endif
+// per wave, token blocks per pass, and the longest segment it takes (the
+// tiled kernel takes the longer ones)
+constexpr int kHybNW = 4, kHybMB = 2, kHybSplit = 32;
 // m-tiles per group in the tiled kernel's tile order
-#ifndef MOE_TILE_GM
-#define MOE_TILE_GM 8
-#endif
+constexpr int kTileGM = 8;
 // tiled kernel (f32 / bf16): WN x WM waves of 64 weight rows x MBW token
-// blocks, stages of weight prefetch, workgroups per CU for 4-wave groups
-#ifndef MOE_TILE_WN
-#define MOE_TILE_WN 4
-#endif
-#ifndef MOE_TILE_WM
-#define MOE_TILE_WM 1
-#endif
-#ifndef MOE_TILE_MBW
-#define MOE_TILE_MBW 8
-#endif
-#ifndef MOE_TILE_WPF
-#define MOE_TILE_WPF 1
-#endif
-#ifndef MOE_TILE_OCC
-#define MOE_TILE_OCC 2
-#endif
-// workgroups per CU the MX-fp8 tiled kernel is compiled for
-#ifndef MOE_TILE_OCC_MX
-#define MOE_TILE_OCC_MX 2
-#endif
-// token rows per tile of the MX-fp8 tiled kernel: 96 covers the ~171 rows
-// an expert gets at 4096 tokens (top-8 of 192) in two m-tiles with 11%
-// padding, where 128 pads by 33%
-#ifndef MOE_TILE_TM_MX
-#define MOE_TILE_TM_MX 96
-#endif
+// blocks, stages of weight prefetch, workgroups per CU
+constexpr int kTileWN = 4, kTileWM = 1, kTileMBW = 8, kTileWPF = 1, kTileOcc = 2;
+// token rows per tile of the 8- and 4-bit tiled kernel: 96 covers the ~171
+// rows an expert gets at 4096 tokens (top-8 of 192) in two m-tiles with 11%
+// padding, where 128 pads by 33%; two workgroups per CU
+constexpr int kTileTMMx = 96, kTileOccMx = 2;
 
-namespace moe {
 
 
 // ----------------------------------------------------------------------------- skinny
@@ -110,10 +63,9 @@ namespace moe {
 // consecutive weight blocks, wave w takes NW of them over the whole K axis.
 // KSW == 4: the four waves share the same NW blocks and take every fourth K
 // chunk each; their partial sums meet in LDS and are added in wave order
-// (fixed, so results are deterministic).  With PF = 1 each wave keeps two
-// register sets and loads chunk c + 1 while the matrix cores work on chunk
-// c; with PF = 0 latency is hidden by occupancy instead (fewer registers per
-// wave, more waves per SIMD), which suits the many-expert launches.
+// (fixed, so results are deterministic).  Load latency is hidden by
+// occupancy (few registers per wave, several waves per SIMD) rather than by
+// double-buffered registers, which measured slower at decode.
 
 template <int F, int NW, int MB>
 struct SkinnyBuf {
@@ -121,7 +73,7 @@ struct SkinnyBuf {
   uint32_t ws[NW], ts[MB];
 };
 
-template <int F, int EPI, int OT, int NW, int MB, int KSW, int PF>
+template <int F, int EPI, int OT, int NW, int MB, int KSW>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int nbtot = g.N >> 4;
@@ -216,22 +168,10 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
         }
     };
 
-    if constexpr (PF) {
-      SkinnyBuf<F, NW, MB> b0, b1;
-      if (k0 < kcn) load(b0, k0);
-      for (int kc = k0; kc < kcn; kc += 2 * KSW) {
-        if (kc + KSW < kcn) load(b1, kc + KSW);
-        compute(b0);
-        if (kc + KSW >= kcn) break;
-        if (kc + 2 * KSW < kcn) load(b0, kc + 2 * KSW);
-        compute(b1);
-      }
-    } else {
-      for (int kc = k0; kc < kcn; kc += KSW) {
-        SkinnyBuf<F, NW, MB> b0;
-        load(b0, kc);
-        compute(b0);
-      }
+    for (int kc = k0; kc < kcn; kc += KSW) {
+      SkinnyBuf<F, NW, MB> b0;
+      load(b0, kc);
+      compute(b0);
     }
 
     if constexpr (KSW == 4) {
@@ -316,17 +256,12 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
   // over all XCDs.
   const int ntn = g.N / TN;
   const int total = tile_scan<TM>(g, cum) * ntn;
-#if MOE_TILE_MAP == 0
   const int per_xcd = (total + 7) >> 3;
   const int local = blockIdx.x >> 3;
   const int logical = (blockIdx.x & 7) * per_xcd + local;
   if (local >= per_xcd || logical >= total) return;
-#else
-  const int logical = blockIdx.x;
-  if (logical >= total) return;
-#endif
   int e, row0, row_end, nt;
-  tile_locate<TM, MOE_TILE_GM>(g, cum, ntn, logical, e, row0, row_end, nt);
+  tile_locate<TM, kTileGM>(g, cum, ntn, logical, e, row0, row_end, nt);
   float fa, fb;
   tensor_factors<F, EPI>(g, e, fa, fb);
 
@@ -524,12 +459,12 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
 // ----------------------------------------------------------------------------- dispatch
 
 // lds_pad: dynamic LDS per workgroup, which only caps residency.
-template <int F, int EPI, int OT, int NW, int MB, int KSW, int PF = 0>
+template <int F, int EPI, int OT, int NW, int MB, int KSW>
 static hipError_t launch_skinny(const GemmArgs &g, int segs, hipStream_t stream, int lds_pad = 0) {
   constexpr int BPW = (KSW == 4) ? NW : 4 * NW;
   const int nbtot = g.N / 16;
   if (nbtot % BPW) return hipErrorInvalidValue;
-  gemm_skinny_kernel<F, EPI, OT, NW, MB, KSW, PF>
+  gemm_skinny_kernel<F, EPI, OT, NW, MB, KSW>
       <<<segs * (nbtot / BPW), 256, lds_pad, stream>>>(g);
   return hipGetLastError();
 }
@@ -575,36 +510,36 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
   } else if (g.rows <= 64 * g.k_route) {
     // at most T <= 64 rows per expert: the streaming kernel takes them all
     constexpr bool eight = (F == FMT_FP8 || F == FMT_MX8);
-    constexpr int SNW0 = (F == FMT_MX4 && EPI == EPI_SWIGLU) ? MOE_SKINNY_NW_MX4
-                         : eight                              ? MOE_SKINNY_NW_8BIT
-                                                              : MOE_SKINNY_NW;
-    const int pad = eight ? MOE_SKINNY_LDS_PAD_8BIT : MOE_SKINNY_LDS_PAD;
+    constexpr int SNW0 = (F == FMT_MX4 && EPI == EPI_SWIGLU) ? kSkinnyNWMx4
+                         : eight                              ? kSkinnyNW8
+                                                              : kSkinnyNW;
+    const int pad = eight ? kSkinnyLdsPad8 : kSkinnyLdsPad;
     // a SwiGLU epilogue needs gate/up pairs (2 weight blocks), an
     // MX-quantising one whole 32-column blocks (4)
     constexpr int SNW = (EPI == EPI_SWIGLU && OT == FMT_MX8 && SNW0 < 4)   ? 4
                         : (EPI == EPI_SWIGLU && SNW0 < 2) ? 2
                                                           : SNW0;
-    if (per <= 16) return launch_skinny<F, EPI, OT, SNW, 1, 1, MOE_SKINNY_PF>(g, segs, stream, pad);
+    if (per <= 16) return launch_skinny<F, EPI, OT, SNW, 1, 1>(g, segs, stream, pad);
     if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
     return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
   } else {
-    // experts of at most MOE_HYB_SPLIT rows go to the streaming kernel, the
+    // experts of at most kHybSplit rows go to the streaming kernel, the
     // longer ones to the tiled kernel (the split is applied on the device,
     // where the counts are)
-    g.split = MOE_HYB_SPLIT;
-    constexpr int HNW = (EPI == EPI_SWIGLU && OT == FMT_MX8) ? 4 : MOE_HYB_NW;
-    hipError_t err = launch_skinny<F, EPI, OT, HNW, MOE_HYB_MB, 1>(g, segs, stream);
+    g.split = kHybSplit;
+    constexpr int HNW = (EPI == EPI_SWIGLU && OT == FMT_MX8) ? 4 : kHybNW;
+    hipError_t err = launch_skinny<F, EPI, OT, HNW, kHybMB, 1>(g, segs, stream);
     if (err != hipSuccess) return err;
   }
   if constexpr (is_mx<F> || F == FMT_FP8) {
-    return launch_tile<F, EPI, OT, 4, 1, MOE_TILE_TM_MX / 16, 1, MOE_TILE_OCC_MX>(g, total_rows,
+    return launch_tile<F, EPI, OT, 4, 1, kTileTMMx / 16, 1, kTileOccMx>(g, total_rows,
                                                                                   stream);
   } else {
     // two waves per SIMD: one workgroup of WN x WM = 8 waves, or two of 4
-    constexpr int WN = MOE_TILE_WN, WM = MOE_TILE_WM;
-    constexpr int OCC = (WN * WM >= 8) ? 1 : MOE_TILE_OCC;
+    constexpr int WN = kTileWN, WM = kTileWM;
+    constexpr int OCC = (WN * WM >= 8) ? 1 : kTileOcc;
     if (g.N % (64 * WN) == 0)
-      return launch_tile<F, EPI, OT, WN, WM, MOE_TILE_MBW, MOE_TILE_WPF, OCC>(g, total_rows,
+      return launch_tile<F, EPI, OT, WN, WM, kTileMBW, kTileWPF, OCC>(g, total_rows,
                                                                                stream);
     return launch_tile<F, EPI, OT, 4, 1, 8, 1, 2>(g, total_rows, stream);
   }
