@@ -9,7 +9,7 @@ JSON line whose headline is the Hy3 decode batch; every workload has its own
 object under "workloads".
 
 Timing: each timed step is bracketed by HIP events on the caller's stream;
-before every step (outside the bracket) a 1 GiB fill evicts L2 and the
+before every step (outside the bracket) a 1 GiB read evicts L2 and the
 256 MB MALL.  Reported: the median step, with p10 and p90.
 
   roofline     the dominant kernel (the routed gate/up + SwiGLU GEMM): its
@@ -260,8 +260,11 @@ def main():
     flush_buf = None if a.no_flush else torch.empty(1 << 30, dtype=torch.uint8, device=dev)
 
     def flush():
+        # a read of 1 GiB on the caller's stream, outside the bracket: it
+        # evicts L2 and the MALL and leaves them holding clean lines (a fill
+        # would leave dirty lines whose write-back lands inside the next step)
         if flush_buf is not None:
-            flush_buf.fill_(1)      # a fill kernel on the caller's stream, outside the bracket
+            torch.amax(flush_buf)
 
     def timed(step_fn, steps, warmup):
         for _ in range(warmup):
