@@ -40,7 +40,16 @@ namespace moe {
 //  * E2M1 weights: 8 blocks per wave for the gate/up GEMM, whose blocks are
 //    half as large (0.212 -> 0.205 ms against 4), 2 for the down GEMM, at 5
 //    workgroups per CU (layer 0.367 -> 0.363 ms against 4 blocks at 3).
-constexpr int kSkinnyLdsPad = 30000, kSkinnyLdsPad8 = 45000;
+//  * bf16 and fp32 at up to 16 rows per expert: each workgroup's four waves
+//    split the K axis of the same 2 blocks (partial sums added in LDS in
+//    wave order), 3 workgroups per CU (35000 bytes of padding beside the
+//    6 KiB reduction buffer): four times as many, shorter workgroups, so the
+//    launch's last round leaves HBM idle for less time (Hy3 decode layer
+//    1.041 ms against 1.084 with whole-K waves; 4, 5 or 6 workgroups per
+//    CU: 1.044 / 1.048 / 1.075 ms; 4 blocks per workgroup: 1.061).  The same
+//    split measured slower for E2M1 (W4A8 decode 0.396 ms against 0.373)
+//    and no better for 8-bit weights, which keep whole-K waves.
+constexpr int kSkinnyLdsPad = 30000, kSkinnyLdsPad8 = 45000, kSkinnyLdsPadKs = 35000;
 constexpr int kSkinnyNW = 2, kSkinnyNW8 = 4, kSkinnyNWMx4 = 8;
 // streaming kernel for the short segments of a mixed launch: weight blocks
 // per wave, token blocks per pass, and the longest segment it takes (the
@@ -519,7 +528,11 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     constexpr int SNW = (EPI == EPI_SWIGLU && OT == FMT_MX8 && SNW0 < 4)   ? 4
                         : (EPI == EPI_SWIGLU && SNW0 < 2) ? 2
                                                           : SNW0;
-    if (per <= 16) return launch_skinny<F, EPI, OT, SNW, 1, 1>(g, segs, stream, pad);
+    if (per <= 16) {
+      if constexpr (F == FMT_BF16 || F == FMT_F32)
+        return launch_skinny<F, EPI, OT, SNW, 1, 4>(g, segs, stream, kSkinnyLdsPadKs);
+      return launch_skinny<F, EPI, OT, SNW, 1, 1>(g, segs, stream, pad);
+    }
     if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
     return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
   } else {
