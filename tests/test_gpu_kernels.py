@@ -486,3 +486,23 @@ def test_grouped_ffn_uneven_segments(orc, ctx):
     idx[:, 1] = np.where(np.arange(500) % 5 == 0, 3, 1)
     err = _ffn_case(orc, ctx, w, 500, tag=0, idx=idx)
     assert err <= TOL["bf16"], err
+
+
+@pytest.mark.parametrize("dtype,H,I_", [("bf16", 512, 256), ("f32", 256, 128)])
+def test_grouped_ffn_skewed_row_classes(orc, ctx, dtype, H, I_):
+    # a skewed batch in one grouped GEMM: experts of up to 32 rows go to the
+    # streaming kernel, longer ones to the tiled kernel; sizes at both sides of
+    # that boundary and of the 64- and 128-row tile edges, an empty expert and
+    # one of several m-tiles
+    counts = [1, 5, 32, 33, 47, 64, 65, 100, 128, 129, 0, 250, 40, 60, 36, 62]
+    E, k = len(counts), 2
+    T = sum(counts) // k
+    # expert list sorted by expert; token t takes entries t and t + T, which
+    # differ because no expert holds more than T rows
+    L = np.repeat(np.arange(E, dtype=np.int32), counts)
+    idx = np.stack([L[:T], L[T:]], axis=1)
+    assert (idx[:, 0] != idx[:, 1]).all()
+    w = I.Workload("classes", T=T, H=H, E=E, k=k, I=I_, Is=I_, dtype=dtype)
+    err = _ffn_case(orc, ctx, w, T, tag=4, idx=idx)
+    print("[ffn skewed row classes] %s T=%d rel err %.3g" % (dtype, T, err))
+    assert err <= TOL[dtype], err
