@@ -55,6 +55,12 @@ constexpr int kSkinnyNW = 2, kSkinnyNW8 = 4, kSkinnyNWMx4 = 8;
 // per wave, token blocks per pass, and the longest segment it takes (the
 // tiled kernel takes the longer ones)
 constexpr int kHybNW = 4, kHybMB = 2, kHybSplit = 32;
+// The mixed launch is used only when the experts average at most kHybMean
+// rows (beyond that the tiled kernel takes every expert: on the skewed Hy4
+// batch, 64 rows per expert on average with 88 of 256 experts at 32 rows or
+// fewer, 1.98 ms against 2.02 with the mixed launch, 2.04 / 2.05 with the
+// split at 24 / 16 rows and 2.52 at 48)
+constexpr int kHybMean = 32;
 // m-tiles per group in the tiled kernel's tile order
 constexpr int kTileGM = 8;
 // tiled kernel (f32 / bf16): WN x WM waves of 64 weight rows x MBW token
@@ -535,7 +541,7 @@ static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t strea
     }
     if (per <= 32) return launch_skinny<F, EPI, OT, 4, 2, 1>(g, segs, stream);
     return launch_skinny<F, EPI, OT, 4, 4, 1>(g, segs, stream);
-  } else {
+  } else if (per <= kHybMean) {
     // experts of at most kHybSplit rows go to the streaming kernel, the
     // longer ones to the tiled kernel (the split is applied on the device,
     // where the counts are)

@@ -427,21 +427,21 @@ def _ffn_case(orc, ctx, w, T, tag, shared=False, idx=None):
     ("f32", 256, 128, 4, 2, 300),       # tiled kernel, several m-tiles + ragged tail
     ("bf16", 512, 256, 12, 4, 30),      # streaming
     ("bf16", 512, 256, 3, 2, 400),      # tiled
-    ("bf16", 512, 256, 12, 2, 300),     # mixed: short experts streamed, long ones tiled
-    ("f32", 256, 128, 12, 2, 300),      # mixed, fp32
+    ("bf16", 512, 256, 24, 2, 360),     # mixed (at most 32 rows per expert on average): short experts streamed, long ones tiled
+    ("f32", 256, 128, 24, 2, 360),      # mixed, fp32
     # MX at the workloads' intermediate size: the scaled fp8 MFMA sums with
     # ~1e-5 relative error, so a few SwiGLU outputs land one E4M3 code away
     # from the oracle's; at I = 1536 that stays far inside 3e-2, at small I
     # one such code on a large h element is a larger share of max|y|
     ("mxfp8", 1024, 1536, 12, 4, 30),   # streaming, MX
     ("mxfp8", 1024, 1536, 3, 2, 400),   # tiled, MX
-    ("mxfp8", 1024, 1536, 12, 2, 300),  # mixed, MX
+    ("mxfp8", 1024, 1536, 24, 2, 360),  # mixed, MX
     ("w4a8", 1024, 1536, 12, 4, 30),    # streaming, MXFP4 weights x MX-fp8 tokens
     ("w4a8", 1024, 1536, 3, 2, 400),    # tiled, W4A8
-    ("w4a8", 1024, 1536, 12, 2, 300),   # mixed, W4A8
+    ("w4a8", 1024, 1536, 24, 2, 360),   # mixed, W4A8
     ("fp8", 1024, 1536, 12, 4, 30),     # streaming, static per-tensor FP8
     ("fp8", 1024, 1536, 3, 2, 400),     # tiled, FP8
-    ("fp8", 1024, 1536, 12, 2, 300),    # mixed, FP8
+    ("fp8", 1024, 1536, 24, 2, 360),    # mixed, FP8
 ])
 def test_grouped_ffn_parity(orc, ctx, dtype, H, I_, E, k, T):
     w = I.Workload("ffn", T=T, H=H, E=E, k=k, I=I_, Is=I_, dtype=dtype)
@@ -488,14 +488,23 @@ def test_grouped_ffn_uneven_segments(orc, ctx):
     assert err <= TOL["bf16"], err
 
 
+SKEWED_COUNTS = {
+    # more than 32 rows per expert on average: the tiled kernel takes every
+    # expert; sizes at the 64- and 128-row tile edges, an empty expert and one
+    # of several m-tiles
+    "tiled": [1, 5, 32, 33, 47, 64, 65, 100, 128, 129, 0, 250, 40, 60, 36, 62],
+    # at most 32 on average: experts of up to 32 rows go to the streaming
+    # kernel and the longer ones to the tiled kernel in the same GEMM
+    "mixed": [0] * 8 + [1, 2, 3, 5, 8, 13, 21, 31, 32, 33, 34, 40, 64, 65, 100, 129] + [2] * 7 + [3],
+}
+
+
 @pytest.mark.parametrize("dtype,H,I_", [("bf16", 512, 256), ("f32", 256, 128)])
-def test_grouped_ffn_skewed_row_classes(orc, ctx, dtype, H, I_):
-    # a skewed batch in one grouped GEMM: experts of up to 32 rows go to the
-    # streaming kernel, longer ones to the tiled kernel; sizes at both sides of
-    # that boundary and of the 64- and 128-row tile edges, an empty expert and
-    # one of several m-tiles
-    counts = [1, 5, 32, 33, 47, 64, 65, 100, 128, 129, 0, 250, 40, 60, 36, 62]
+@pytest.mark.parametrize("counts_name", ["tiled", "mixed"])
+def test_grouped_ffn_skewed_row_classes(orc, ctx, dtype, H, I_, counts_name):
+    counts = SKEWED_COUNTS[counts_name]
     E, k = len(counts), 2
+    assert sum(counts) % k == 0 and (sum(counts) / E > 32) == (counts_name == "tiled")
     T = sum(counts) // k
     # expert list sorted by expert; token t takes entries t and t + T, which
     # differ because no expert holds more than T rows
@@ -504,5 +513,5 @@ def test_grouped_ffn_skewed_row_classes(orc, ctx, dtype, H, I_):
     assert (idx[:, 0] != idx[:, 1]).all()
     w = I.Workload("classes", T=T, H=H, E=E, k=k, I=I_, Is=I_, dtype=dtype)
     err = _ffn_case(orc, ctx, w, T, tag=4, idx=idx)
-    print("[ffn skewed row classes] %s T=%d rel err %.3g" % (dtype, T, err))
+    print("[ffn skewed row classes] %s %s T=%d rel err %.3g" % (counts_name, dtype, T, err))
     assert err <= TOL[dtype], err
