@@ -1,7 +1,9 @@
 """Benchmark of one Hunyuan-style MoE layer forward pass on one MI355X.
 
 A step is one moe_layer_forward call (gating, permutation, routed grouped
-SwiGLU GEMM, shared expert on the side stream, combine) over one batch of
+SwiGLU GEMM, shared expert -- on the side stream where that pays, else on
+the caller's stream, folded into the routed GEMMs where it can be -- and
+combine) over one batch of
 synthetic tokens, with weights and inputs already resident in HBM.  The
 default run times the five workloads (tiny fp32, Hy3 decode T = 64, Hy3
 prefill T = 8192, Hy4-shape skewed T = 2048, MX-fp8 T = 4096) and prints one
@@ -12,7 +14,8 @@ Timing: each timed step is bracketed by HIP events on the caller's stream;
 before every step (outside the bracket) a 1 GiB read evicts L2 and the
 256 MB MALL.  Reported: the median step, with p10 and p90.
 
-  roofline     the dominant kernel (the routed gate/up + SwiGLU GEMM): its
+  roofline     the dominant kernel (the routed gate/up + SwiGLU GEMM, with the
+               shared expert's gate/up when that is folded into it): its
                algorithmic bytes (HBM-bound workloads) or flops (prefill) per
                launch over its duration, timed with HIP events recorded
                around it on its own stream (median of profiled steps)
@@ -375,17 +378,26 @@ def main():
         gu_bytes = touched * 2 * w.I * w.H * ew + T * w.H * xb + P * w.I * ab
         gu_flops = 2.0 * P * 2 * w.I * w.H
         gu_ms = stages["gate_up"]
+        # a layer whose shared expert shows no time of its own ran it inside
+        # the routed GEMMs (one more segment, on the caller's stream): the
+        # gate/up kernel then also does the shared expert's gate/up work
+        folded = w.Is > 0 and stages["shared_gate_up"] == 0.0
+        gu_kernel = "routed gate/up + SwiGLU grouped GEMM"
+        if folded:
+            gu_bytes += 2 * w.Is * w.H * ews + T * w.Is * ab
+            gu_flops += 2.0 * T * 2 * w.Is * w.H
+            gu_kernel += " (with the shared expert's gate/up as one more segment)"
         mfma_peak = (FP8_PEAK_TFLOPS if eight else FP32_PEAK_TFLOPS if w.dtype == "f32"
                      else BF16_PEAK_TFLOPS)
         if w.name in MFMA_BOUND:
             ach = gu_flops / (gu_ms * 1e-3) / 1e12
-            roof = {"bound": "mfma", "kernel": "routed gate/up + SwiGLU grouped GEMM",
+            roof = {"bound": "mfma", "kernel": gu_kernel,
                     "achieved": round(ach, 1), "peak": mfma_peak, "unit": "TFLOP/s",
                     "frac": round(ach / mfma_peak, 4), "traffic": None,
                     "kernel_ms": round(gu_ms, 4), "algorithmic_flops": gu_flops}
         else:
             ach = gu_bytes / (gu_ms * 1e-3) / 1e9
-            roof = {"bound": "hbm", "kernel": "routed gate/up + SwiGLU grouped GEMM",
+            roof = {"bound": "hbm", "kernel": gu_kernel,
                     "achieved": round(ach, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                     "frac": round(ach / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
                     "kernel_ms": round(gu_ms, 4), "algorithmic_bytes": int(gu_bytes)}

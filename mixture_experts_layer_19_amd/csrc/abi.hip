@@ -197,11 +197,14 @@ moe_status check_ctx(moe_ctx *ctx) {
 }
 
 // One expert FFN (routed or shared) given activations already in the expert
-// format (xa: x itself for f32/bf16, the MX codes for MX-fp8).
+// format (xa: x itself for f32/bf16, the MX codes for MX-fp8).  sh_y, sh_h
+// (routed f32 / bf16 call only, shared and routed experts of one format and
+// intermediate size): the shared expert rides along as one more segment of
+// the routed grouped GEMMs, writing its h to sh_h and its output to sh_y.
 hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *xa,
                const uint8_t *xs, int T, const int32_t *sorted_src, const int32_t *offsets,
                void *y, void *h, uint8_t *hs, hipStream_t s, StageTimer *tm = nullptr,
-               hipEvent_t after_first = nullptr) {
+               hipEvent_t after_first = nullptr, void *sh_y = nullptr, void *sh_h = nullptr) {
   const int st1 = shared ? MOE_STAGE_SHARED_GATE_UP : MOE_STAGE_GATE_UP;
   const int st2 = shared ? MOE_STAGE_SHARED_DOWN : MOE_STAGE_DOWN;
   const int F = weight_fmt(d, shared);
@@ -232,6 +235,13 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g1.out = h;
   g1.out_scale = hs;
   g1.n_out = I;
+  if (sh_y) {
+    g1.w2 = (const uint8_t *)w->sh_gate_up;
+    g1.a2 = (const uint8_t *)xa;
+    g1.a2_bytes = g1.a_bytes;
+    g1.out2 = sh_h;
+    g1.rows2 = T;
+  }
   // static per-tensor FP8: weight scales [E][2], the x scale, and the scale
   // h is quantised with (then the down GEMM's activation scale)
   const float sh = shared ? d->fp8_sh_h_scale : d->fp8_h_scale;
@@ -270,6 +280,13 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   g2.out = y;
   g2.out_scale = nullptr;
   g2.n_out = H;
+  if (sh_y) {
+    g2.w2 = (const uint8_t *)w->sh_down;
+    g2.a2 = (const uint8_t *)sh_h;
+    g2.a2_bytes = (long long)T * I * (long long)eb;
+    g2.out2 = sh_y;
+    g2.rows2 = T;
+  }
   if (F == FMT_FP8) {
     g2.w_tscale = (const float *)(shared ? w->sh_down_scale : w->down_scale);
     g2.w_scale = nullptr;
@@ -656,13 +673,21 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   //    Hy4-skew (64 rows per expert) 2.084 against 2.120, MX-fp8 at 4096
   //    tokens (171 rows per expert) 1.393 against 1.433.
   // Otherwise the shared expert runs on the caller's stream, in the same
-  // place in the order.
+  // place in the order.  There, for f32 / bf16 experts whose shared and
+  // routed intermediate sizes agree, its two GEMMs are folded into the
+  // routed ones as one more segment at the end of the tile list: its tiles
+  // fill the routed GEMM's last, partial round instead of a launch of their
+  // own (Hy3 prefill: 3.130 ms against 3.167; gate/up with the shared
+  // expert's 1.780 ms against 1.602 + 0.208).
   const size_t shared_weight_bytes =
       (size_t)3 * H * desc->shared_inter * elem_bytes(weight_fmt_dtype(desc, 1));
   const bool side_pays = shared_weight_bytes >= ((size_t)1 << 20) &&
                          (long long)T * k < 256LL * E;
   const bool two = has_shared && ctx->side && ctx->side != s && side_pays;
   const bool early = two && (mx || fp8_act(desc)) && T <= kSharedEarlyT;
+  const bool fold = has_shared && !two && !mx && !fp8_act(desc) &&
+                    desc->shared_inter == desc->inter &&
+                    weight_fmt(desc, 0) == weight_fmt(desc, 1) && E < 1024;
   auto shared_expert = [&]() -> hipError_t {
     hipStream_t ss = two ? ctx->side : s;
     hipError_t e;
@@ -691,9 +716,10 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   MOE_TRY(tm.stop(MOE_STAGE_PERMUTE, s), "timing");
   MOE_TRY(ffn(desc, w, 0, xa, xs, T, src, offsets, b + L.y, b + L.h,
               mx ? (uint8_t *)b + L.hs : nullptr, s, &tm,
-              two && !early ? ctx->ev_ready : nullptr),
+              two && !early ? ctx->ev_ready : nullptr, fold ? b + L.z : nullptr,
+              fold ? b + L.sh_h : nullptr),
           "routed experts");
-  if (has_shared && !early) MOE_TRY(shared_expert(), "shared expert");
+  if (has_shared && !early && !fold) MOE_TRY(shared_expert(), "shared expert");
   // Join, then FinalizeRouting + shared add.
   if (two) MOE_TRY(hipStreamWaitEvent(s, ctx->ev_done, 0), "main stream wait");
   const int of = fmt_of(desc->out_dtype);

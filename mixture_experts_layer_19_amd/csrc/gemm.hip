@@ -210,7 +210,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
           for (int n = 0; n < NW; ++n) col[n] = acc[n][i];
           const int r = mbase + 16 * i + (lane & 15);
-          epilogue<F, EPI, OT, NW>(col, nb0, r, r < s1, g, lane, fa, fb);
+          epilogue<F, EPI, OT, NW>(col, nb0, r, r < s1, g, lane, fa, fb, g.out);
         }
       }
       __syncthreads();
@@ -221,7 +221,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(GemmArgs g) {
 #pragma unroll
         for (int n = 0; n < NW; ++n) col[n] = acc[n][i];
         const int r = mbase + 16 * i + (lane & 15);
-        epilogue<F, EPI, OT, NW>(col, nb0, r, r < s1, g, lane, fa, fb);
+        epilogue<F, EPI, OT, NW>(col, nb0, r, r < s1, g, lane, fa, fb, g.out);
       }
     }
   }
@@ -277,6 +277,9 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
   if (local >= per_xcd || logical >= total) return;
   int e, row0, row_end, nt;
   tile_locate<TM, kTileGM>(g, cum, ntn, logical, e, row0, row_end, nt);
+  // the extra segment (bf16 / fp32 only): its own weights, rows and output
+  constexpr bool kExtra = (F == FMT_BF16 || F == FMT_F32);
+  const bool xseg = kExtra && g.offsets && e == g.E;
   float fa, fb;
   tensor_factors<F, EPI>(g, e, fa, fb);
 
@@ -288,12 +291,13 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
   // scalar and each lane keeps one offset per stream instead of a 64-bit
   // pointer, which leaves the vector registers to the accumulators and the
   // operands in flight.
-  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(g.w + (size_t)e * g.w_expert_stride,
+  const __amdgpu_buffer_rsrc_t wrs = make_rsrc(xseg ? g.w2 : g.w + (size_t)e * g.w_expert_stride,
                                               (uint32_t)g.w_expert_stride);
   constexpr int TF = tok_fmt<F>;         // token-side format
   constexpr int WB = wblock_bytes<F>;    // bytes per weight block
   const uint32_t wvoff = (uint32_t)(nb0 * kcn) * WB + lane * 16;
-  const __amdgpu_buffer_rsrc_t trs = make_rsrc(g.a, (uint32_t)g.a_bytes);
+  const __amdgpu_buffer_rsrc_t trs =
+      xseg ? make_rsrc(g.a2, (uint32_t)g.a2_bytes) : make_rsrc(g.a, (uint32_t)g.a_bytes);
   // MX scales: weight scale pairs [row block][chunk][lane] of this expert,
   // token scale bytes [row][K / 32]
   __amdgpu_buffer_rsrc_t wsrs = wrs, tsrs = trs;
@@ -314,7 +318,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     const int rl = idx >> 3, seg = idx & 7;
     int r = row0 + rl;
     if (r >= row_end) r = row_end - 1;
-    tvoff[i] = (uint32_t)(token_of(g, r) * g.a_row_bytes) + seg * 16;
+    tvoff[i] = (uint32_t)((xseg ? (long long)r : token_of(g, r)) * g.a_row_bytes) + seg * 16;
     tdst[i] = (rl >> 4) * 2048 + (seg >> 2) * 1024 + tslot(rl & 15, seg & 3, seg >> 2) * 16;
   }
   // MX token scales: entry idx = tid + NTH i is (token block idx / 64, lane idx % 64)
@@ -467,7 +471,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
 #pragma unroll
     for (int n = 0; n < NBW; ++n) col[n] = acc[n][m];
     const int r = row0 + (wm * MBW + m) * 16 + (lane & 15);
-    epilogue<F, EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane, fa, fb);
+    epilogue<F, EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane, fa, fb, xseg ? g.out2 : g.out);
   }
 }
 
@@ -490,7 +494,8 @@ template <int F, int EPI, int OT, int WN, int WM, int MBW, int WPF, int OCC>
 static hipError_t launch_tile(GemmArgs g, int total_rows, hipStream_t stream) {
   constexpr int TN = 64 * WN, TM = 16 * WM * MBW;
   if (g.N % TN != 0) return hipErrorInvalidValue;
-  const int mtiles = g.offsets ? (total_rows + TM - 1) / TM + g.E : (g.rows + TM - 1) / TM;
+  const int mtiles = g.offsets ? (total_rows + TM - 1) / TM + g.E + (g.rows2 + TM - 1) / TM
+                               : (g.rows + TM - 1) / TM;
   g.mt_upper = mtiles;
   // upper bound on the tiles, rounded up to whole rounds of the 8 XCDs
   long long nblocks = (long long)mtiles * (g.N / TN);
@@ -503,6 +508,30 @@ static hipError_t launch_tile(GemmArgs g, int total_rows, hipStream_t stream) {
 template <int F, int EPI, int OT>
 static hipError_t run_gemm(const GemmArgs &g0, int total_rows, hipStream_t stream) {
   GemmArgs g = g0;
+  if (g.rows2 > 0) {
+    // The extra segment rides in the tiled launch (filling the routed
+    // GEMM's last, partial round of tiles) where that launch takes long
+    // segments; otherwise it runs as a GEMM of its own.
+    const bool tiled = (F == FMT_BF16 || F == FMT_F32) && g.offsets && g.E < 1024 &&
+                       g.rows > 64 * g.k_route && g.a_bytes <= 0xFFFFFFFFll &&
+                       g.a2_bytes <= 0xFFFFFFFFll && g.w_expert_stride <= 0xFFFFFFFFull &&
+                       g.N % (64 * kTileWN) == 0;
+    if (!tiled) {
+      GemmArgs gx = g0;
+      gx.w = g0.w2;
+      gx.a = g0.a2;
+      gx.a_bytes = g0.a2_bytes;
+      gx.sorted_src = nullptr;
+      gx.offsets = nullptr;
+      gx.rows = g0.rows2;
+      gx.E = 1;
+      gx.out = g0.out2;
+      gx.rows2 = 0;
+      const hipError_t err = run_gemm<F, EPI, OT>(gx, gx.rows, stream);
+      if (err != hipSuccess) return err;
+      g.rows2 = 0;
+    }
+  }
   const int segs = g.offsets ? g.E : 1;
   // rows per segment: the mean for expert segments, all rows for one segment
   const int per = g.offsets ? (total_rows + segs - 1) / segs : total_rows;

@@ -11,14 +11,15 @@ __device__ __forceinline__ float silu(float v) { return v / (1.0f + expf(-v)); }
 
 // ----------------------------------------------------------------------------- epilogue
 // acc[n] (n < NB) is one 16-token column of NB consecutive 16-row weight
-// blocks starting at global block nb0.  Lane: token row `row` (stores only if
-// `valid`), features 4 * (lane / 16) + r of each block.  Static per-tensor
+// blocks starting at global block nb0.  Lane: token row `row` of out (stores
+// only if `valid`), features 4 * (lane / 16) + r of each block.  Static per-tensor
 // FP8 (F == FMT_FP8) first multiplies the gate (and plain) sums by fa and the
 // up sums by fb: the product of the expert's weight scale and the
 // activation scale.
 template <int F, int EPI, int OT, int NB>
 __device__ __forceinline__ void epilogue(f32x4 (&acc)[NB], int nb0, long long row, bool valid,
-                                         const GemmArgs &g, int lane, float fa, float fb) {
+                                         const GemmArgs &g, int lane, float fa, float fb,
+                                         void *out) {
   const int c4 = 4 * (lane >> 4);
   if constexpr (F == FMT_FP8) {
 #pragma unroll
@@ -35,7 +36,7 @@ __device__ __forceinline__ void epilogue(f32x4 (&acc)[NB], int nb0, long long ro
       for (int r = 0; r < 4; ++r) c |= e4m3_rne((silu(acc[2 * q][r]) * acc[2 * q + 1][r]) / sh) << (8 * r);
       if (valid) {
         const long long col = (long long)(nb0 / 2 + q) * 16 + c4;
-        *(uint32_t *)((uint8_t *)g.out + row * g.n_out + col) = c;
+        *(uint32_t *)((uint8_t *)out + row * g.n_out + col) = c;
       }
     }
   } else if constexpr (EPI == EPI_SWIGLU) {
@@ -65,7 +66,7 @@ __device__ __forceinline__ void epilogue(f32x4 (&acc)[NB], int nb0, long long ro
         }
         if (valid) {
           const int hb = nb0 / 2 + 2 * u;          // first h block (16 columns)
-          uint8_t *o = (uint8_t *)g.out + row * g.n_out + hb * 16 + c4;
+          uint8_t *o = (uint8_t *)out + row * g.n_out + hb * 16 + c4;
           *(uint32_t *)o = c0;
           *(uint32_t *)(o + 16) = c1;
           if (lane < 16) g.out_scale[row * (g.n_out / 32) + hb / 2] = (uint8_t)sb;
@@ -83,9 +84,9 @@ __device__ __forceinline__ void epilogue(f32x4 (&acc)[NB], int nb0, long long ro
           uint2 p;
           p.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
           p.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
-          *(uint2 *)((uint16_t *)g.out + row * g.n_out + col) = p;
+          *(uint2 *)((uint16_t *)out + row * g.n_out + col) = p;
         } else {
-          *(float4 *)((float *)g.out + row * g.n_out + col) = make_float4(v[0], v[1], v[2], v[3]);
+          *(float4 *)((float *)out + row * g.n_out + col) = make_float4(v[0], v[1], v[2], v[3]);
         }
       }
     }
@@ -98,9 +99,9 @@ __device__ __forceinline__ void epilogue(f32x4 (&acc)[NB], int nb0, long long ro
         uint2 p;
         p.x = (uint32_t)f32_to_bf16_rne(acc[n][0]) | ((uint32_t)f32_to_bf16_rne(acc[n][1]) << 16);
         p.y = (uint32_t)f32_to_bf16_rne(acc[n][2]) | ((uint32_t)f32_to_bf16_rne(acc[n][3]) << 16);
-        *(uint2 *)((uint16_t *)g.out + row * g.n_out + col) = p;
+        *(uint2 *)((uint16_t *)out + row * g.n_out + col) = p;
       } else {
-        *(float4 *)((float *)g.out + row * g.n_out + col) =
+        *(float4 *)((float *)out + row * g.n_out + col) =
             make_float4(acc[n][0], acc[n][1], acc[n][2], acc[n][3]);
       }
     }
@@ -127,10 +128,12 @@ __device__ __forceinline__ long long token_of(const GemmArgs &g, int r) {
 
 // ----------------------------------------------------------------------------- tile map
 // m-tiles are numbered expert by expert (TM rows each, the last one of an
-// expert ragged).  tile_scan computes, from the segment offsets alone (they
-// stay on the device), cum[e] = m-tiles of experts 0..e and returns the total;
-// tile_locate below maps a tile index to its expert, rows and n-tile.  At
-// least 256 threads; cum holds >= 1024 ints.
+// expert ragged), then those of the extra segment (index E, rows2 rows) if
+// there is one.  tile_scan computes, from the segment offsets alone (they
+// stay on the device), cum[e] = m-tiles of segments 0..e and returns the
+// total; tile_locate below maps a tile index to its segment, rows and n-tile.
+// At least 256 threads; cum holds >= 1024 ints (E + 1 <= 1024 with an extra
+// segment).
 template <int TM>
 __device__ int tile_scan(const GemmArgs &g, int *cum) {
   if (!g.offsets) return (g.rows + TM - 1) / TM;
@@ -141,7 +144,7 @@ __device__ int tile_scan(const GemmArgs &g, int *cum) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int ex = tid * 4 + i;
-      int c = ex < g.E ? g.offsets[ex + 1] - g.offsets[ex] : 0;
+      int c = ex < g.E ? g.offsets[ex + 1] - g.offsets[ex] : (ex == g.E ? g.rows2 : 0);
       if (c <= g.split) c = 0;               // left to the streaming kernel
       run += (c + TM - 1) / TM;
       v[i] = run;
@@ -164,7 +167,7 @@ __device__ int tile_scan(const GemmArgs &g, int *cum) {
     for (int i = 0; i < 4; ++i) cum[tid * 4 + i] = before + v[i];
   }
   __syncthreads();
-  return cum[g.E - 1];
+  return cum[g.E - 1 + (g.rows2 > 0 ? 1 : 0)];
 }
 
 // Tile order inside one expert: its m-tiles are taken in groups of GM; a
@@ -173,8 +176,8 @@ __device__ int tile_scan(const GemmArgs &g, int *cum) {
 // neighbours in dispatch order (they start within moments of each other
 // and walk K in step, so the weights come from HBM once and from L2 for the
 // others), and the n-tiles that share a token tile are at most GM apart.
-// Tile t -> expert e, rows [row0, row_end) of its segment (row0 is the
-// first row of the m-tile), n-tile nt.
+// Tile t -> segment e (E: the extra segment, whose rows count from 0), rows
+// [row0, row_end) of it (row0 is the first row of the m-tile), n-tile nt.
 template <int TM, int GM>
 __device__ void tile_locate(const GemmArgs &g, const int *cum, int ntn, int t, int &e, int &row0,
                             int &row_end, int &nt) {
@@ -186,7 +189,7 @@ __device__ void tile_locate(const GemmArgs &g, const int *cum, int ntn, int t, i
     seg0 = 0;
     seg1 = g.rows;
   } else {
-    int lo = 0, hi = g.E - 1;
+    int lo = 0, hi = g.E - 1 + (g.rows2 > 0 ? 1 : 0);
     while (lo < hi) {
       int mid = (lo + hi) >> 1;
       if (cum[mid] * ntn > t) hi = mid;
@@ -195,8 +198,13 @@ __device__ void tile_locate(const GemmArgs &g, const int *cum, int ntn, int t, i
     e = lo;
     first = lo ? cum[lo - 1] : 0;
     mte = cum[lo] - first;
-    seg0 = g.offsets[lo];
-    seg1 = g.offsets[lo + 1];
+    if (lo < g.E) {
+      seg0 = g.offsets[lo];
+      seg1 = g.offsets[lo + 1];
+    } else {
+      seg0 = 0;
+      seg1 = g.rows2;
+    }
   }
   const int local = t - first * ntn;
   const int grp = local / (GM * ntn), in = local - grp * (GM * ntn);

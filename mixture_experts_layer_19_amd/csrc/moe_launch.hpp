@@ -31,6 +31,16 @@ struct GemmArgs {
   int mt_upper;               // tile kernel: m-tiles in the grid
   int split;                  // > 0: the streaming kernel takes segments of at most
                               // `split` rows and the tiled kernel the longer ones
+  // bf16 / fp32 only: one more segment after the E expert segments when
+  // rows2 > 0 (the shared expert folded into the routed GEMM): rows2 rows
+  // read straight from a2 (no gather; a2_bytes bytes, a_row_bytes per row)
+  // against the weight set w2 (one expert's layout and stride), written to
+  // out2 ([rows2][n_out])
+  const uint8_t *w2;
+  const uint8_t *a2;
+  long long a2_bytes;
+  void *out2;
+  int rows2;
   // static per-tensor FP8 only: weight scales per expert ([E][2] gate, up for
   // SwiGLU; [E] otherwise), the token-side activation scale, and the scale
   // the SwiGLU output is quantised with

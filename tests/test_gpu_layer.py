@@ -118,8 +118,11 @@ def test_layer_zero_tokens_is_a_noop():
     assert torch.all(out == 7.0)
 
 
-@pytest.mark.parametrize("name", ["tiny", "hy3_decode", "w4a8_decode", "fp8_decode"])
+@pytest.mark.parametrize("name", ["tiny", "hy3_decode", "w4a8_decode", "fp8_decode", "hy4_skew"])
 def test_layer_is_deterministic_and_stream_independent(name):
+    # (Hy4-skew: with the side stream its shared expert runs as GEMMs of its
+    # own; on the caller's stream it rides in the routed GEMMs as one more
+    # segment; both give the same bits)
     w = I.workload(name)
     lay = device_layer(w)
     xg, _ = I.x_input(w)
