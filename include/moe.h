@@ -238,7 +238,10 @@ MOE_API moe_status moe_combine(moe_ctx *ctx, const moe_desc *desc /* host */, co
  * not for a shared expert under 1 MiB of weights (launch-bound layers), and
  * not at 256 or more rows per routed expert (T * k >= 256 * E, where every
  * GEMM is bound by the matrix cores); there the shared expert runs on
- * `stream` in the same place.  On return `stream` has been made to wait for
+ * `stream` in the same place -- for f32 / bf16 experts with I_s equal to I
+ * (and fewer than 1024 experts) as one more segment of the routed grouped
+ * GEMMs, whose last partial round of tiles it fills; the result is the same
+ * bit for bit.  On return `stream` has been made to wait for
  * the side stream, so work queued on `stream` afterwards sees the finished
  * layer.
  *   x [T,H] (act_dtype), out [T,H] (out_dtype).
