@@ -108,6 +108,23 @@ def test_layer_largest_expert_count_and_top_k(orc, dtype, E, k, T):
     _check_layer(orc, "maxes", w=w)
 
 
+@pytest.mark.parametrize("dtype,T,I_,Is", [
+    # T * k >= 256 * E, so no side stream: the shared expert rides in the
+    # routed tiled GEMMs as one more segment (ragged last m-tile)
+    ("bf16", 1100, 256, 256), ("f32", 1100, 128, 128),
+    # the same with a shared intermediate size of its own: separate GEMMs on
+    # the caller's stream
+    ("bf16", 1100, 256, 512),
+    # a small batch (streaming kernels only): the shared segment runs as a
+    # GEMM of its own inside the routed stage
+    ("bf16", 40, 256, 256),
+])
+def test_layer_shared_expert_placements(orc, dtype, T, I_, Is):
+    H = 512 if dtype == "bf16" else 256
+    w = I.Workload("placement", T=T, H=H, E=8, k=2, I=I_, Is=Is, dtype=dtype)
+    _check_layer(orc, "placement", w=w)
+
+
 def test_layer_zero_tokens_is_a_noop():
     w = I.workload("tiny")
     lay = device_layer(w)
