@@ -96,9 +96,7 @@ __global__ __launch_bounds__(256) void router_logits_kernel(const XT *__restrict
 // Hy3 shape: decode (T = 64) gating 24.2 -> 20.8 us; at T = 8192 the split
 // repeated by every token tile costs more than the separate pass (95 ->
 // 116 us), so large batches keep it.
-#ifndef MOE_ROUTER_FUSED_SPLIT_T
-#define MOE_ROUTER_FUSED_SPLIT_T 256
-#endif
+constexpr int kRouterFusedSplitT = 256;
 
 // bf16 activations: matrix-core kernels.  W_r is split exactly into three
 // bf16 terms, w = hi + mid + lo (each remainder is exact in fp32 and the last
@@ -470,7 +468,7 @@ hipError_t launch_route(const void *x, int x_is_bf16, const float *Wr, const flo
   const RoutePlan p = router_plan(T, H, E, x_is_bf16);
   const int ksn = p.ksn;
   if (x_is_bf16) {
-    const bool fused = T <= MOE_ROUTER_FUSED_SPLIT_T;
+    const bool fused = T <= kRouterFusedSplitT;
     const size_t pbytes = (((size_t)ksn * T * E * sizeof(float)) + 255) & ~(size_t)255;
     uint4 *wsplit = (uint4 *)((char *)part + pbytes);
     if (!fused) {
