@@ -60,7 +60,7 @@ def parse():
     ap.add_argument("--profile-steps", type=int, default=10)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle sample")
     ap.add_argument("--no-graph", action="store_true",
                     help="skip timing the batch replayed from a captured HIP graph")
@@ -465,7 +465,7 @@ def main():
         t1 = time.perf_counter()
         run(n)
         first = time.perf_counter() - t1
-        reps = int(max(1, min(100, a.cpu_seconds / max(first, 1e-3))))
+        reps = int(max(1, min(1000, a.cpu_seconds / max(first, 1e-3))))
         t1 = time.perf_counter()
         for _ in range(reps):
             run(n)
