@@ -73,6 +73,9 @@ def parse():
                     help="also run a plain 1 GiB device copy (HBM counter calibration)")
     ap.add_argument("--trace-summary", metavar="DIR",
                     help="summarise the rocprofv3 kernel trace under DIR and exit")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("WORKLOAD", "FETCH_DIR", "WRITE_DIR", "JSON"),
+                    help="write the gate/up traffic file of WORKLOAD from rocprofv3 FETCH_SIZE and "
+                         "WRITE_SIZE runs and the FETCH_SIZE run's bench line, and exit")
     ap.add_argument("--counter-summary", metavar="DIR", nargs="+",
                     help="summarise rocprofv3 --pmc outputs under DIR(s) and exit")
     return ap.parse_args()
@@ -98,12 +101,11 @@ def cpu_model() -> str:
 
 
 def measured_traffic(workload: str):
-    """HBM bytes per launch of the decode gate/up kernel from the committed
-    rocprofv3 FETCH_SIZE / WRITE_SIZE summary, or None when the kernel's
+    """HBM bytes per launch of the workload's gate/up kernel from its committed
+    rocprofv3 FETCH_SIZE / WRITE_SIZE summary (profiles/<workload>_gate_up_traffic.txt,
+    written by --traffic-summary), or None when there is none or the GEMM
     source has changed since those counters were taken."""
-    if workload != "hy3_decode":
-        return None
-    path = os.path.join(ROOT, "profiles", "hy3_decode_gate_up_traffic.txt")
+    path = os.path.join(ROOT, "profiles", "%s_gate_up_traffic.txt" % workload)
     if not os.path.exists(path):
         return None
     kv = {}
@@ -115,6 +117,74 @@ def measured_traffic(workload: str):
     if kv.get("source_sha256") != gemm_source_sha256():
         return None
     return int(kv["traffic_bytes"])
+
+
+def traffic_summary(workload: str, fetch_dir: str, write_dir: str, bench_json: str) -> None:
+    """The traffic file of the workload's gate/up kernel: the largest-grid
+    grouped GEMM dispatch with the SwiGLU epilogue (template arguments
+    <format, 0, ...>) in two rocprofv3 --pmc runs of bench.py (FETCH_SIZE,
+    then WRITE_SIZE, both with --copy-calib), calibrated by the 1 GiB device
+    copy of the same runs, against the algorithmic bytes the counter run's
+    bench line reports."""
+    import csv
+    import glob
+    import re
+
+    def load(d, counter):
+        vals = {}
+        for f in sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r["Counter_Name"] != counter:
+                        continue
+                    name = re.sub(r"\(.*$", "", r["Kernel_Name"]).replace("void ", "").replace("moe::", "")
+                    vals.setdefault((name, int(r["Grid_Size"])), []).append(float(r["Counter_Value"]))
+        return vals
+
+    fv, wv = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    gemm = [k for k in fv if re.match(r"gemm_(skinny|tile)_kernel<\d+, 0,", k[0])]
+    if not gemm:
+        sys.exit("no gate/up GEMM dispatch in %s" % fetch_dir)
+    key = max(gemm, key=lambda k: k[1])
+    def copy_kib(vals):
+        # mean over the dispatches of the largest copy (the 1 GiB calibration)
+        grids = [g for (n, g) in vals if n == "__amd_rocclr_copyBuffer"]
+        if not grids:
+            return 0.0
+        v = vals[("__amd_rocclr_copyBuffer", max(grids))]
+        return sum(v) / len(v)
+
+    copy_f, copy_w = copy_kib(fv), copy_kib(wv)
+    if copy_f <= 0 or copy_w <= 0 or key not in wv:
+        sys.exit("the runs need --copy-calib and the kernel in both counter passes")
+    ff, fw = (1 << 30) / (copy_f * 1024.0), (1 << 30) / (copy_w * 1024.0)
+    fk, wk = sum(fv[key]) / len(fv[key]), sum(wv[key]) / len(wv[key])
+    traffic = int(round(fk * 1024 * ff + wk * 1024 * fw))
+    with open(bench_json) as fh:
+        line = json.loads(fh.read().strip().splitlines()[-1])
+    alg = int(line["roofline"]["algorithmic_bytes"])
+    cmd = ("bench.py --workload %s --steps 3 --warmup 1 --profile-steps 1 --no-cpu --no-parity "
+           "--no-graph --no-flush --copy-calib" % workload)
+    print("# HBM traffic of the gate/up kernel of the %s workload" % workload)
+    print("# Commands (from /tmp, TMPDIR=/tmp), one counter per run, then this summary:")
+    print("#   rocprofv3 --pmc FETCH_SIZE --output-format csv -d <f> -o p -- python3 %s > <f>.json" % cmd)
+    print("#   rocprofv3 --pmc WRITE_SIZE --output-format csv -d <w> -o p -- python3 %s" % cmd)
+    print("#   python3 bench.py --traffic-summary %s <f> <w> <f>.json" % workload)
+    print("# Calibration: the runs copy 1 GiB device-to-device; the counters read FETCH_SIZE %.1f KiB"
+          % copy_f)
+    print("# and WRITE_SIZE %.1f KiB for it, so bytes = FETCH_SIZE * 1024 * %.4f and WRITE_SIZE * 1024 * %.4f."
+          % (copy_w, ff, fw))
+    print("# Values are KiB per dispatch, averaged over %d dispatches.  Algorithmic bytes of the" % len(fv[key]))
+    print("# kernel (from the counter run's bench line): %d; the measured traffic is %.4f x that." %
+          (alg, traffic / alg))
+    print("kernel: %s grid %d" % (key[0], key[1]))
+    print("source_sha256: %s" % gemm_source_sha256())
+    print("fetch_kib: %.1f" % fk)
+    print("write_kib: %.1f" % wk)
+    print("fetch_factor: %.4f" % ff)
+    print("write_factor: %.4f" % fw)
+    print("algorithmic_bytes: %d" % alg)
+    print("traffic_bytes: %d" % traffic)
 
 
 # ----------------------------------------------------------------------------- trace summary
@@ -245,6 +315,9 @@ def main():
         return
     if a.counter_summary:
         counter_summary(a.counter_summary)
+        return
+    if a.traffic_summary:
+        traffic_summary(*a.traffic_summary)
         return
     if a.gpus != 1:
         print("bench.py measures one GPU: the library runs the whole MoE layer on a single "
@@ -393,8 +466,9 @@ def main():
             ach = gu_flops / (gu_ms * 1e-3) / 1e12
             roof = {"bound": "mfma", "kernel": gu_kernel,
                     "achieved": round(ach, 1), "peak": mfma_peak, "unit": "TFLOP/s",
-                    "frac": round(ach / mfma_peak, 4), "traffic": None,
-                    "kernel_ms": round(gu_ms, 4), "algorithmic_flops": gu_flops}
+                    "frac": round(ach / mfma_peak, 4), "traffic": measured_traffic(w.name),
+                    "kernel_ms": round(gu_ms, 4), "algorithmic_flops": gu_flops,
+                    "algorithmic_bytes": int(gu_bytes)}
         else:
             ach = gu_bytes / (gu_ms * 1e-3) / 1e9
             roof = {"bound": "hbm", "kernel": gu_kernel,
