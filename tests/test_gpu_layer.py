@@ -125,6 +125,27 @@ def test_layer_shared_expert_placements(orc, dtype, T, I_, Is):
     _check_layer(orc, "placement", w=w)
 
 
+@pytest.mark.parametrize("case", [
+    # one expert, top-1: every token goes to it with weight rho (s / s = 1)
+    dict(dtype="bf16", T=100, E=1, k=1),
+    # k = E: every token uses every expert
+    dict(dtype="bf16", T=70, E=8, k=8),
+    dict(dtype="f32", T=300, E=4, k=4),
+    # no shared expert
+    dict(dtype="bf16", T=100, E=8, k=2, Is=0),
+    dict(dtype="mxfp8", T=100, E=8, k=2, Is=0),
+    # route_norm off: the weights are rho * sigmoid scores as they are
+    dict(dtype="bf16", T=100, E=8, k=2, route_norm=False, rho=1.0),
+], ids=["e1k1", "k_eq_e", "k_eq_e_f32", "no_shared", "no_shared_mx", "no_route_norm"])
+def test_layer_degenerate_routing(orc, case):
+    c = dict(case)
+    dtype = c.pop("dtype")
+    H, Iw = (512, 256) if dtype in ("mxfp8", "w4a8", "fp8") else (256, 128)
+    Is = c.pop("Is", Iw)
+    w = I.Workload("degenerate", H=H, I=Iw, Is=Is, dtype=dtype, **c)
+    _check_layer(orc, "degenerate", w=w)
+
+
 def test_layer_zero_tokens_is_a_noop():
     w = I.workload("tiny")
     lay = device_layer(w)
