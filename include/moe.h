@@ -14,12 +14,18 @@
  *
  * computed as Gating -> InitRouting (permutation) -> grouped GEMM ->
  * FinalizeRouting (weighted combine) -> add of the always-on shared expert,
- * which runs on a second stream joined by an event.
+ * which runs on a second stream joined by an event where that pays (see
+ * moe_layer_forward).
  *
  * Conventions for every call:
  *  - Pointers are DEVICE pointers unless marked "host".  The caller owns all
  *    memory; the library never allocates device memory after moe_ctx_create
  *    (which creates two events) and never frees caller memory.
+ *  - Activations, outputs, workspaces, router weights and packed expert
+ *    weights are read or written with 16-byte vector accesses and must start
+ *    16-byte aligned (any allocation is); a misaligned one returns
+ *    MOE_ERR_INVALID_ARG.  The sources of moe_mx_quantize, moe_fp8_quantize
+ *    and moe_pack_experts and moe_permute's topk_idx may be unaligned.
  *  - Streams are hipStream_t handles passed as void* (NULL = the null stream).
  *    Calls enqueue work on the given stream and return without synchronising;
  *    results are ready when that stream reaches the point of the call.

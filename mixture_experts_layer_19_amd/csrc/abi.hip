@@ -299,9 +299,18 @@ hipError_t ffn(const moe_desc *d, const moe_weights *w, int shared, const void *
   return err;
 }
 
+// Device arrays the kernels read or write with 16-byte vector accesses
+// (activations, outputs, workspaces, packed weights) must start 16-byte
+// aligned; NULL passes (the callers check presence separately).
+inline bool al16(const void *p) { return ((uintptr_t)p & 15) == 0; }
+
 bool weights_ok(const moe_desc *d, const moe_weights *w, int need_router, int need_routed,
                 int need_shared) {
   if (!w) return false;
+  if (!al16(w->router_w) || !al16(w->gate_up) || !al16(w->down) || !al16(w->sh_gate_up) ||
+      !al16(w->sh_down) || !al16(w->gate_up_scale) || !al16(w->down_scale) ||
+      !al16(w->sh_gate_up_scale) || !al16(w->sh_down_scale))
+    return false;
   const bool mx = mx_act(d) || fp8_act(d);     // both need the scale arrays
   if (need_router && !w->router_w) return false;
   if (need_routed && (!w->gate_up || !w->down || (mx && (!w->gate_up_scale || !w->down_scale))))
@@ -458,6 +467,8 @@ moe_status moe_pack_experts(const moe_desc *desc, int shared, int src_dtype, con
   const bool mx = mx_act(desc) || fp8_act(desc);
   if (!gate || !up || !down || !gate_up_out || !down_out) return MOE_ERR_INVALID_ARG;
   if (mx && (!gate_up_scale_out || !down_scale_out)) return MOE_ERR_INVALID_ARG;
+  if (!al16(gate_up_out) || !al16(down_out) || !al16(gate_up_scale_out) || !al16(down_scale_out))
+    return MOE_ERR_INVALID_ARG;
   const int F = weight_fmt(desc, shared);
   const bool f8 = F == FMT_FP8;
   hipStream_t s = (hipStream_t)stream;
@@ -504,6 +515,7 @@ moe_status moe_route(moe_ctx *ctx, const moe_desc *desc, const void *x, int32_t 
   if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !router_w || !topk_idx || !topk_w || !ws) return MOE_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(router_w) || !al16(ws)) return MOE_ERR_INVALID_ARG;
   Layout L = layout(desc, T, MOE_WS_ROUTE);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipError_t err = launch_route(x, desc->act_dtype == MOE_BF16, router_w, router_bias,
@@ -545,6 +557,7 @@ moe_status moe_grouped_ffn(moe_ctx *ctx, const moe_desc *desc, const moe_weights
   if (T == 0 || (shared && desc->shared_inter == 0)) return MOE_OK;
   if (!x || !y || !ws || !weights_ok(desc, w, 0, !shared, shared)) return MOE_ERR_INVALID_ARG;
   if (!shared && (!sorted_src || !expert_offsets)) return MOE_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(y) || !al16(ws)) return MOE_ERR_INVALID_ARG;
   Layout L = layout(desc, T, shared ? MOE_WS_SHARED_FFN : MOE_WS_GROUPED_FFN);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;
@@ -581,6 +594,7 @@ moe_status moe_combine(moe_ctx *ctx, const moe_desc *desc, const void *y, const 
   if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!y || !dest || !topk_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!al16(y) || !al16(shared_out) || !al16(out)) return MOE_ERR_INVALID_ARG;
   const int of = fmt_of(desc->out_dtype);
   hipError_t err = launch_combine(y, of, dest, topk_w, shared_out, T, desc->hidden, desc->top_k,
                                   out, of, (hipStream_t)stream);
@@ -609,6 +623,7 @@ moe_status moe_layer_forward(moe_ctx *ctx, const moe_desc *desc, const moe_weigh
   if (too_many_pairs(desc, T)) return MOE_ERR_UNSUPPORTED;
   if (T == 0) return MOE_OK;
   if (!x || !out || !ws || !weights_ok(desc, w, 1, 1, 1)) return MOE_ERR_INVALID_ARG;
+  if (!al16(x) || !al16(out) || !al16(ws)) return MOE_ERR_INVALID_ARG;
   Layout L = layout(desc, T, MOE_WS_LAYER);
   if (ws_bytes < L.total) return MOE_ERR_WORKSPACE;
   hipStream_t s = (hipStream_t)stream;

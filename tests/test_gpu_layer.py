@@ -211,6 +211,29 @@ def test_layer_graph_replay_matches_eager_and_oracle(orc, name):
             assert err <= TOL[w.dtype], (rep, err)
 
 
+def test_layer_rejects_misaligned_buffers():
+    # x, out or the workspace off a 16-byte boundary: rejected on the host
+    # before anything is enqueued; the aligned call then runs as usual
+    w = I.workload("tiny")
+    lay = device_layer(w)
+    xg, _ = I.x_input(w)
+    xd = to_device(xg)
+    ws = lay.workspace(w.T)
+    out = torch.empty((w.T, w.H), dtype=lay.out_dtype(), device="cuda")
+    n = w.T * w.H
+    xm = torch.zeros(n + 4, dtype=xd.dtype, device="cuda")[1:1 + n].view(w.T, w.H)
+    xm.copy_(xd)
+    om = torch.zeros(n + 4, dtype=out.dtype, device="cuda")[1:1 + n].view(w.T, w.H)
+    wsm = torch.empty(ws.numel() + 16, dtype=torch.uint8, device="cuda")[4:4 + ws.numel()]
+    for xa, oa, wa in [(xm, out, ws), (xd, om, ws), (xd, out, wsm)]:
+        with pytest.raises(B.MoeError) as ei:
+            B.moe_layer_forward(lay.ctx, lay.desc, lay.weights, xa, w.T, oa, wa, wa.numel())
+        assert ei.value.status == B.MOE_ERR_INVALID_ARG
+    B.moe_layer_forward(lay.ctx, lay.desc, lay.weights, xd, w.T, out, ws, ws.numel())
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all()
+
+
 def test_layer_workspace_too_small():
     w = I.workload("tiny")
     lay = device_layer(w)
