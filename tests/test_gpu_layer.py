@@ -178,7 +178,7 @@ def test_layer_is_deterministic_and_stream_independent(name):
     assert torch.equal(a, c)
 
 
-@pytest.mark.parametrize("name", ["tiny", "hy3_decode", "w4a8_decode"])
+@pytest.mark.parametrize("name", ["tiny", "hy3_decode", "w4a8_decode", "fp8_decode", "hy4_skew"])
 def test_layer_graph_replay_matches_eager_and_oracle(orc, name):
     # one forward captured as a HIP graph (both streams), replayed on three
     # different batches with eager calls and synchronizations in between:
@@ -205,7 +205,10 @@ def test_layer_graph_replay_matches_eager_and_oracle(orc, name):
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out_static, eager), "replay %d differs from the eager call" % rep
-        if rep < 3:
+        # every replay equals its eager call bit for bit; the oracle checks
+        # each batch's first replay (only the first batch's beyond 64 tokens,
+        # to bound the oracle's time)
+        if rep < 3 and (w.T <= 64 or i == 0):
             err = compare_layer(orc, w, hosts[i], to_numpy(out_static), _gpu_idx(lay, w, w.T),
                                 np.arange(w.T), label="%s graph replay %d" % (name, i))
             assert err <= TOL[w.dtype], (rep, err)
