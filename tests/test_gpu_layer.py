@@ -183,7 +183,7 @@ def test_layer_graph_replay_matches_eager_and_oracle(orc, name):
     # one forward captured as a HIP graph (both streams), replayed on three
     # different batches with eager calls and synchronizations in between:
     # every replay equals the eager result for the same batch bit for bit,
-    # and matches the oracle on every token of that batch
+    # and the first replays match the oracle on every token
     w = I.workload(name)
     lay = device_layer(w)
     xg0, x0 = I.x_input(w)
