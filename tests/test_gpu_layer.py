@@ -178,13 +178,18 @@ def test_layer_is_deterministic_and_stream_independent(name):
     assert torch.equal(a, c)
 
 
-@pytest.mark.parametrize("name", ["tiny", "hy3_decode", "w4a8_decode", "fp8_decode", "hy4_skew"])
+# a small layer on both streams (2.4 MB of shared weights) whose experts all
+# go to the tiled kernel (37.5 rows each on average)
+GRAPH_TILED = I.Workload("graph_tiled", T=300, H=512, E=16, k=2, I=768, Is=768, dtype="bf16")
+
+
+@pytest.mark.parametrize("name", ["tiny", "hy3_decode", "w4a8_decode", "fp8_decode", "graph_tiled"])
 def test_layer_graph_replay_matches_eager_and_oracle(orc, name):
     # one forward captured as a HIP graph (both streams), replayed on three
     # different batches with eager calls and synchronizations in between:
     # every replay equals the eager result for the same batch bit for bit,
     # and the first replays match the oracle on every token
-    w = I.workload(name)
+    w = GRAPH_TILED if name == "graph_tiled" else I.workload(name)
     lay = device_layer(w)
     xg0, x0 = I.x_input(w)
     # three batches, exact in the input format: the batch, its rows reversed,
