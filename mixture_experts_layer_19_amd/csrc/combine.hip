@@ -13,22 +13,30 @@
 namespace moe {
 
 constexpr int kMaxK = 16;
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Eight elements of y or the shared output, widened to fp32.  Both are read
+// exactly once, so the loads are non-temporal: they do not displace cached
+// lines (Hy3 prefill combine 0.131 -> 0.112 ms, MX-fp8 at T = 4096 0.067 ->
+// 0.061 ms); the output keeps ordinary stores, so whatever reads it next
+// finds it in the caches.
 template <bool BF16>
 __device__ __forceinline__ void load8(const void *base, long long off, float (&v)[8]) {
   if constexpr (BF16) {
-    uint4 u = *(const uint4 *)((const uint16_t *)base + off);
-    uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const u32x4 u = __builtin_nontemporal_load((const u32x4 *)((const uint16_t *)base + off));
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      v[2 * i] = __uint_as_float(w[i] << 16);
-      v[2 * i + 1] = __uint_as_float(w[i] & 0xFFFF0000u);
+      v[2 * i] = __uint_as_float(u[i] << 16);
+      v[2 * i + 1] = __uint_as_float(u[i] & 0xFFFF0000u);
     }
   } else {
-    const float4 *p = (const float4 *)((const float *)base + off);
-    float4 a = p[0], b = p[1];
-    v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-    v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+    const f32x4 *p = (const f32x4 *)((const float *)base + off);
+    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = a[i];
+      v[4 + i] = b[i];
+    }
   }
 }
 
