@@ -243,13 +243,19 @@ def trace_summary(d: str) -> None:
 
 
 def gemm_source_sha256() -> str:
-    """SHA-256 of the grouped GEMM sources (to tie counter readings to a build)."""
+    """SHA-256 of the grouped GEMM sources with comments and whitespace
+    removed (to tie counter readings to the code they were taken with; a
+    change of comments leaves it as it is)."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in ("mixture_experts_layer_19_amd/csrc/gemm.hip",
               "mixture_experts_layer_19_amd/csrc/gemm_common.hpp",
               "mixture_experts_layer_19_amd/csrc/moe_common.hpp"):
-        h.update(open(os.path.join(ROOT, f), "rb").read())
+        text = open(os.path.join(ROOT, f)).read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 

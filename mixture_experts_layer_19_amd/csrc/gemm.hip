@@ -9,16 +9,24 @@
 //
 // Two kernels, chosen per launch from the expected rows per expert:
 //  * gemm_skinny -- few rows per expert (decode).  Weight-streaming: each wave
-//    owns NW 16-row weight blocks of one expert over the whole K axis and
-//    reads them straight from HBM into registers (1 KiB contiguous per wave
-//    access); the expert's <= 16*MB token rows are read per chunk (they stay
-//    in L2).  No LDS, no barriers.  Untouched experts exit at once.
+//    owns NW 16-row weight blocks of one expert and reads them straight from
+//    HBM into registers with non-temporal loads (1 KiB contiguous per wave
+//    access), over the whole K axis or, with KSW = 4, over a quarter of it
+//    (the four waves' partial sums then added in LDS in wave order); the
+//    expert's <= 16*MB token rows are read per chunk (they stay in L2).
+//    Untouched experts exit at once.
 //  * gemm_tile -- many rows per expert (prefill).  Workgroup tile of TN
 //    weight rows x TM token rows, K staged through LDS half a chunk at a time
 //    (double-buffered, one barrier per stage), register prefetch of the next
 //    stage.  The m-tile -> (expert, rows) map is computed on the device from
 //    the segment offsets, so no host synchronisation is needed; the grid is
-//    sized from an upper bound and surplus workgroups exit.
+//    sized from an upper bound and surplus workgroups exit.  For f32 / bf16
+//    it can take one more segment after the experts (the shared expert, with
+//    its own weights, rows and output).
+// Dispatch (run_gemm): batches of at most 64 tokens use gemm_skinny alone;
+// larger ones with at most 32 rows per expert on average send the experts of
+// up to 32 rows to gemm_skinny and the rest to gemm_tile; beyond that
+// gemm_tile takes every expert.
 //
 // Both kernels take the weight format as a template parameter: fp32, bf16,
 // MX-fp8, E2M1 weights against MX-fp8 tokens (W4A8), or E4M3 with static
