@@ -242,20 +242,24 @@ def trace_summary(d: str) -> None:
               % (busy / 1e3, 100.0 * ov / max(busy, 1)))
 
 
+def _code_text(text: str) -> str:
+    """C++ source with comments removed and whitespace collapsed."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def gemm_source_sha256() -> str:
     """SHA-256 of the grouped GEMM sources with comments and whitespace
     removed (to tie counter readings to the code they were taken with; a
     change of comments leaves it as it is)."""
     import hashlib
-    import re
     h = hashlib.sha256()
     for f in ("mixture_experts_layer_19_amd/csrc/gemm.hip",
               "mixture_experts_layer_19_amd/csrc/gemm_common.hpp",
               "mixture_experts_layer_19_amd/csrc/moe_common.hpp"):
-        text = open(os.path.join(ROOT, f)).read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
+        h.update(_code_text(open(os.path.join(ROOT, f)).read()).encode())
     return h.hexdigest()
 
 
