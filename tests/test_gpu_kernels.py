@@ -231,12 +231,42 @@ def test_route_parity(orc, ctx, name, T):
     assert np.abs(g_w.astype(np.float64).sum(1) - 2.826).max() <= 1e-5
 
 
+def _route_shape_check(orc, ctx, w, tag):
+    xg, x = I.x_input(w)
+    Wr, b = I.router_weight(w), I.router_bias(w)
+    g_idx, g_w = _route_gpu(ctx, w, dev(xg), w.T, dev(Wr), None if b is None else dev(b))
+    o_idx, o_w, scores, gap = orc.route(x, Wr, b, w.k, w.rho, w.route_norm)
+    mism, flips = classify_routing(g_idx, o_idx, scores)
+    print("[route %s] E=%d H=%d T=%d k=%d: %d mismatching, %d tie flips" % (
+        tag, w.E, w.H, w.T, w.k, mism.sum(), flips.sum()))
+    assert not (mism & ~flips).any(), np.nonzero(mism & ~flips)[0][:10]
+    ref_w = o_w.astype(np.float64)
+    if flips.any():
+        ref_w[flips] = orc.route_weights(scores[flips], g_idx[flips], w.rho, w.route_norm)
+    rel = np.abs(g_w.astype(np.float64) - ref_w) / np.abs(ref_w)
+    assert rel.max() <= 1e-6, rel.max()
+
+
+@pytest.mark.parametrize("E,H,T,k", [(200, 2048, 300, 8), (24, 768, 1, 3), (33, 512, 77, 5),
+                                     (16, 4096, 64, 4), (1024, 512, 40, 16)])
+def test_route_parity_f32_shapes(orc, ctx, E, H, T, k):
+    """fp32 routing with K cut into slices of several 32-element blocks
+    (H = 2048, 4096) or of a count that is not a power of two (H = 768: 24
+    blocks in 8 slices), expert counts that are not a multiple of 4 (the
+    top-k pass then strides lanes over the experts) or past 256, ragged
+    token counts."""
+    _route_shape_check(orc, ctx, I.workload("tiny", T=T, H=H, E=E, k=k), "f32")
+
+
 @pytest.mark.parametrize("E,H,T,k,beta", [(40, 512, 77, 6, 0.0), (24, 256, 1, 3, 0.0),
-                                          (200, 768, 300, 8, 0.38), (16, 2048, 129, 4, 0.0)])
+                                          (200, 768, 300, 8, 0.38), (16, 2048, 129, 4, 0.0),
+                                          (33, 512, 77, 5, 0.0), (192, 1024, 20, 8, 0.0)])
 def test_route_parity_bf16_shapes(orc, ctx, E, H, T, k, beta):
     """bf16 routing at expert counts that leave a partial 16-expert block or
-    a partial 64-expert tile, ragged token counts, and K split into slices
-    of different lengths (H / 64 stages)."""
+    a partial 64-expert tile, or are not a multiple of 4, ragged token
+    counts, and K split into slices of different lengths (H / 64 stages;
+    H = 768 and 1024 at small T: slices of at most four stages, whose loads
+    all go out at once)."""
     w = I.workload("hy3_decode", T=T, H=H, E=E, k=k, zipf_beta=beta)
     xg, x = I.x_input(w)
     Wr, b = I.router_weight(w), I.router_bias(w)
