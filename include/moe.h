@@ -7,7 +7,8 @@
  * walkthrough parts 1-3):
  *
  *   s      = sigmoid(x W_r^T + b)                         gating scores
- *   idx    = the top-k experts of each token by s          (ties: lower index)
+ *   idx    = the top-k experts of each token by s          (ties: lower index;
+ *                                                           a NaN s counts as 0)
  *   w      = rho * s[idx] / sum(s[idx])                    route_norm, scaling
  *   y_e    = W_d,e ( silu(W_g,e x) * (W_u,e x) )           SwiGLU expert FFN
  *   out    = sum_j w_j y_idx_j(x)  +  FFN_shared(x)        combine + shared

@@ -404,14 +404,16 @@ __global__ __launch_bounds__(256) void router_gemm_kernel(const uint16_t *__rest
 
 // --------------------------------------------------------------------------- top-k
 // One wave per token.  Lane l holds experts l, l+64, l+128, ... (up to
-// E <= 64 * kMaxPerLane).  Scores s = fp32(1 / (1 + exp(-z))) are evaluated
-// in fp64 and rounded once.  The selection key of expert e is the 64-bit
-// number bits(s) * 2^32 + (2^32 - 1 - e): scores are never negative, so their
-// bit patterns order like their values, and of two equal scores the lower
-// expert index has the larger key (a NaN score ranks as zero).  k rounds of
-// a wave-wide key maximum pick the selection in key order; the selected
-// scores are summed in slot order in fp64 and each weight rho * s / sum is
-// rounded once to fp32.
+// E <= 64 * kMaxPerLane), or four consecutive ones (PK below).  Scores
+// s = fp32(1 / (1 + exp(-z))) are evaluated in fp64 and rounded once.  The
+// selection key of expert e is the 64-bit number bits(s) * 2^32 +
+// (2^32 - 1 - e): scores are never negative, so their bit patterns order
+// like their values, and of two equal scores the lower expert index has the
+// larger key (a NaN score counts as zero, in the ranking and in the weights,
+// so the selection is always k valid experts).  k rounds of a wave-wide key
+// maximum pick the selection in key order; the selected scores are summed
+// in slot order in fp64 and each weight rho * s / sum is rounded once to
+// fp32.
 
 constexpr int kMaxPerLane = 16;   // E <= 1024
 
