@@ -285,6 +285,26 @@ def test_route_parity_bf16_shapes(orc, ctx, E, H, T, k, beta):
     assert rel.max() <= 1e-6, rel.max()
 
 
+@pytest.mark.parametrize("name", ["tiny", "hy3_decode"])
+def test_route_nan_token_selects_k_valid_experts(ctx, name):
+    """A token whose activations hold a NaN gets NaN logits.  Its scores
+    count as zero, so it selects experts 0 .. k-1 (ties go to the lower
+    index): always k distinct experts in range, which the permutation indexes
+    by.  Every other token's routing is unchanged bit for bit."""
+    w = I.workload(name, T=8)
+    xg, _ = I.x_input(w)
+    Wr, b = I.router_weight(w), I.router_bias(w)
+    bd = None if b is None else dev(b)
+    ref_idx, ref_w = _route_gpu(ctx, w, dev(xg), w.T, dev(Wr), bd)
+    xn = xg.copy()
+    xn[3, 5] = np.float32(np.nan) if xn.dtype == np.float32 else np.uint16(0x7FC0)
+    idx, tw = _route_gpu(ctx, w, dev(xn), w.T, dev(Wr), bd)
+    np.testing.assert_array_equal(idx[3], np.arange(w.k))
+    keep = np.arange(w.T) != 3
+    np.testing.assert_array_equal(idx[keep], ref_idx[keep])
+    np.testing.assert_array_equal(tw[keep], ref_w[keep])
+
+
 def test_route_zero_router_ties_to_lowest_indices(ctx):
     w = I.workload("tiny")
     xg, _ = I.x_input(w)
