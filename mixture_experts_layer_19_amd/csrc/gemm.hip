@@ -473,6 +473,49 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     if (s0 + q.value < nstage) stage_q(s0 + q.value, q);
   });
 
+  if constexpr (EPI == EPI_PLAIN && F == FMT_BF16 && OT == FMT_BF16 && WM == 1 && TN == 256) {
+    // bf16 output of the bf16 GEMMs through the token LDS slots (free after
+    // the last stage): each pass writes RPP rows of the tile there, their
+    // 16-byte segments permuted by row so that the 16 rows of one write hit
+    // distinct banks, then every row leaves as 512 contiguous bytes (prefill
+    // down GEMM 1.078 -> 1.025 ms against the 16-byte stores of epilogue();
+    // the 8-bit kernels keep epilogue(): there this path spills)
+    constexpr int RB = TN * 2, SEGS = RB / 16;
+    constexpr int RPS = TBYTES / RB, RPP = 2 * RPS, MPP = RPP / 16;
+    static_assert(RPP % 16 == 0 && TM % RPP == 0, "epilogue passes");
+    uint16_t *outp = (uint16_t *)(xseg ? g.out2 : g.out);
+    static_for<TM / RPP>([&](auto pc) MOE_INLINE {
+      constexpr int pass = decltype(pc)::value;
+      __syncthreads();
+#pragma unroll
+      for (int mm = 0; mm < MPP; ++mm) {
+        const int rl = mm * 16 + (lane & 15);
+        uint8_t *slot = rl < RPS ? tb0 : tb1;
+        const int r2 = rl < RPS ? rl : rl - RPS;
+#pragma unroll
+        for (int n = 0; n < NBW; ++n) {
+          f32x4 v = acc[n][pass * MPP + mm];
+          if constexpr (F == FMT_FP8) v *= fa;
+          const int cb = ((wn * NBW + n) * 16 + 4 * (lane >> 4)) * 2;
+          uint2 q;
+          q.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
+          q.y = (uint32_t)f32_to_bf16_rne(v[2]) | ((uint32_t)f32_to_bf16_rne(v[3]) << 16);
+          *(uint2 *)(slot + r2 * RB + (((cb >> 4) ^ (r2 & 31)) << 4) + (cb & 15)) = q;
+        }
+      }
+      __syncthreads();
+#pragma unroll
+      for (int i0 = 0; i0 < RPP * SEGS; i0 += NTH) {
+        const int i = i0 + tid;
+        const int rl = i / SEGS, seg = i % SEGS;
+        const uint8_t *slot = rl < RPS ? tb0 : tb1;
+        const int r2 = rl < RPS ? rl : rl - RPS;
+        const uint4 q = *(const uint4 *)(slot + r2 * RB + ((seg ^ (r2 & 31)) << 4));
+        const int row = row0 + pass * RPP + rl;
+        if (row < row_end) *(uint4 *)(outp + (long long)row * g.n_out + nt * TN + seg * 8) = q;
+      }
+    });
+  } else {
 #pragma unroll
   for (int m = 0; m < MBW; ++m) {
     f32x4 col[NBW];
@@ -480,6 +523,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     for (int n = 0; n < NBW; ++n) col[n] = acc[n][m];
     const int r = row0 + (wm * MBW + m) * 16 + (lane & 15);
     epilogue<F, EPI, OT, NBW>(col, nb0, r, r < row_end, g, lane, fa, fb, xseg ? g.out2 : g.out);
+  }
   }
 }
 
