@@ -483,6 +483,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
     constexpr int RB = TN * 2, SEGS = RB / 16;
     constexpr int RPS = TBYTES / RB, RPP = 2 * RPS, MPP = RPP / 16;
     static_assert(RPP % 16 == 0 && TM % RPP == 0, "epilogue passes");
+    static_assert(RPP * SEGS % NTH == 0, "every thread reads whole rounds of segments");
     uint16_t *outp = (uint16_t *)(xseg ? g.out2 : g.out);
     static_for<TM / RPP>([&](auto pc) MOE_INLINE {
       constexpr int pass = decltype(pc)::value;
@@ -494,8 +495,7 @@ __global__ __launch_bounds__(64 * WN * WM, OCC) void gemm_tile_kernel(GemmArgs g
         const int r2 = rl < RPS ? rl : rl - RPS;
 #pragma unroll
         for (int n = 0; n < NBW; ++n) {
-          f32x4 v = acc[n][pass * MPP + mm];
-          if constexpr (F == FMT_FP8) v *= fa;
+          const f32x4 v = acc[n][pass * MPP + mm];
           const int cb = ((wn * NBW + n) * 16 + 4 * (lane >> 4)) * 2;
           uint2 q;
           q.x = (uint32_t)f32_to_bf16_rne(v[0]) | ((uint32_t)f32_to_bf16_rne(v[1]) << 16);
